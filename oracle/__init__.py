@@ -1,0 +1,43 @@
+"""CPU oracle for the 8-bit quantized, optionally block-sparse attention forward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package; the product path never
+calls it and shares no code with it (the HIP kernels, the C ABI and the Python
+binding are written separately and import nothing from here).
+
+Everything here is plain numpy (fp64 unless a step fixes another precision),
+written for reading, not for speed:
+
+* ``exact_attention``     -- the result the method approximates: softmax
+  attention in fp64, optionally restricted to a block mask.
+* ``smooth_quant``        -- the K smoothing and per-block INT8 quantization of
+  Q and K, with optional mean-pooled block vectors.
+* ``block_mask``          -- the mean-pooled block score and the per-query-block
+  keep list.
+* ``emulate_attention``   -- the quantized path step by step: INT8 scores,
+  online base-2 softmax, rounded probabilities, fp64 accumulation.
+
+Sources (the explainer pages these follow):
+
+* SageAttention explainer, aibr.jp/archives/102657, sections 2-3: smooth K,
+  quantize the attention inputs to 8 bits, INT8 matrix products for Q K^T and
+  16-bit products for P V, FlashAttention-style tiling (section 4).
+* ThriftAttention summary, gist.science/ja/paper/2605.23081, technical summary,
+  method: block importance from the dot product of the block mean vectors,
+  top-k block pairs, online softmax merge as in FlashAttention-2.
+* SALE explainer, aibr.jp/archives/118208, sections 1 and 3: a cheap low-bit
+  estimate turned into a block-sparse plan that skips the rest, with the sink
+  (first) and local (diagonal) stripes kept.
+
+Parity pins: every function here is pinned by CPU tests against closed forms,
+invariants, a library routine that computes the same definition, or brute force
+(tests/test_oracle_*.py). The floating-point tail of ``emulate_attention``
+beyond what those pins fix (the exact value of each exp2 rounding) is not
+pinned by any printed value: the pages print no worked example.
+"""
+
+from .rounding import bf16_rne, f16_rne, round_to_dtype  # noqa: F401
+from .quant import (k_channel_mean, quantize_block, smooth_quant,  # noqa: F401
+                    pool_vector_quant)
+from .mask import block_mask, max_keep, select_blocks  # noqa: F401
+from .attention import exact_attention, emulate_attention, softmax_scale_log2  # noqa: F401

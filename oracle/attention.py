@@ -1,0 +1,185 @@
+"""Exact attention and the step-by-step quantized path (oracle; test infrastructure only).
+
+``exact_attention`` is the plain definition the method approximates:
+O = softmax(Q K^T / sqrt(d)) V per (batch, query head), in fp64, with query
+head hq reading kv head hq // (Hq / Hkv), an optional causal mask (key j is
+visible to query i iff j <= i) and an optional block mask (a key is visible
+only when its 64-key block is in the query's 128-query block keep list).
+
+``emulate_attention`` follows the quantized kernel of the SageAttention
+explainer (aibr.jp/archives/102657, sections 2-3: INT8 product for Q K^T, a
+16-bit product for P V, FlashAttention-style tiling per section 4) with the
+online softmax merge of the ThriftAttention summary (gist.science/ja/paper/
+2605.23081, technical summary, method: merged as in FlashAttention-2). Readings
+where the pages are silent:
+
+* per query block of 128 rows and per key tile of ``kv_tile`` keys, ascending:
+  S = q_codes . k_codes^T (exact integers);
+* dequantization folds the softmax temperature and the change to base 2:
+  c = fl32(log2(e) / sqrt(d)), alpha_q = fl32(q_scale * c),
+  alpha = fl32(alpha_q * k_scale[key block]), s = fl32(S * alpha);
+  masked scores are -inf;
+* m_new = max(m_old, rowmax(s)); P = fl32(exp2(fl32(s - m_new)));
+  P_hat = P rounded to nearest-even in V's dtype (the 16-bit operand of the
+  P V product); corr = fl32(exp2(fl32(m_old - m_new)));
+  l = l * corr + sum(P_hat); acc = acc * corr + P_hat V, accumulated in fp64
+  (the kernel accumulates in fp32: the 16-bit products are exact in either);
+* O = round_dtype(fl32(acc / l)); lse = ln(2) * (m + log2(l)), the natural log
+  normalizer of the smoothed, dequantized logits.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .quant import Q_BLOCK, K_BLOCK, _as_f64
+from .rounding import round_to_dtype
+
+LOG2E = 1.4426950408889634
+
+
+def softmax_scale_log2(d: int) -> np.float32:
+    """fl32(log2(e) / sqrt(d)): the scale folded into the INT8 dequantization."""
+    return np.float32(LOG2E / math.sqrt(d))
+
+
+def _kept_keys_mask(kv_idx_row, cnt, N):
+    keep = np.zeros(N, dtype=bool)
+    for j in kv_idx_row[:cnt]:
+        keep[int(j) * K_BLOCK:(int(j) + 1) * K_BLOCK] = True
+    return keep
+
+
+def exact_attention(q, k, v, causal: bool, kv_idx=None, kv_cnt=None, blocks=None):
+    """fp64 softmax attention. Returns (O fp64 [B,Hq,N,d], lse fp64 [B,Hq,N]).
+
+    ``blocks`` optionally restricts the work to a list of (b, hq, i) query
+    blocks; other entries are NaN.
+    """
+    q64, k64, v64 = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, Hq, N, d = q64.shape
+    Hkv = k64.shape[1]
+    group = Hq // Hkv
+    O = np.full((B, Hq, N, d), np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    nqb = N // Q_BLOCK
+    if blocks is None:
+        blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nqb)]
+    inv_sqrt_d = 1.0 / math.sqrt(d)
+    keys = np.arange(N)
+    for b, hq, i in blocks:
+        hk = hq // group
+        r0, r1 = i * Q_BLOCK, (i + 1) * Q_BLOCK
+        s = (q64[b, hq, r0:r1] @ k64[b, hk].T) * inv_sqrt_d
+        vis = np.ones((Q_BLOCK, N), dtype=bool)
+        if causal:
+            vis &= keys[None, :] <= np.arange(r0, r1)[:, None]
+        if kv_idx is not None:
+            vis &= _kept_keys_mask(kv_idx[b, hq, i], kv_cnt[b, hq, i], N)[None, :]
+        s = np.where(vis, s, -np.inf)
+        mx = np.max(s, axis=1, keepdims=True)
+        mx_safe = np.where(np.isfinite(mx), mx, 0.0)
+        p = np.exp(s - mx_safe)
+        den = p.sum(axis=1, keepdims=True)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            O[b, hq, r0:r1] = np.where(den > 0, (p @ v64[b, hk]) / den, 0.0)
+            lse[b, hq, r0:r1] = np.where(den[:, 0] > 0, mx_safe[:, 0] + np.log(den[:, 0]), -np.inf)
+    return O, lse
+
+
+def _kv_tiles_dense(i: int, N: int, causal: bool, kv_tile: int):
+    n_tiles = N // kv_tile
+    if not causal:
+        return list(range(n_tiles))
+    last_key = Q_BLOCK * i + Q_BLOCK - 1
+    return list(range(min(n_tiles, last_key // kv_tile + 1)))
+
+
+def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hkv: int,
+                      kv_idx=None, kv_cnt=None, kv_tile: int = K_BLOCK,
+                      p_dtype: str | None = None, out_dtype: str | None = None,
+                      blocks=None):
+    """The quantized path, step by step.
+
+    q_i8 [B,Hq,N,d] int8, q_scale [B,Hq,N/128] f32, k_i8 [B,Hkv,N,d] int8,
+    k_scale [B,Hkv,N/64] f32, v [B,Hkv,N,d] in the 16-bit dtype (torch tensor
+    or fp64 array). ``kv_idx``/``kv_cnt`` select the sparse path (the kept
+    64-key blocks, ascending); then ``kv_tile`` must be 64.
+    ``p_dtype`` is the dtype P is rounded to ("bf16", "f16", or "f32" for no
+    16-bit rounding); ``out_dtype`` the output's. Both default to V's dtype,
+    which must then be given as a torch tensor.
+
+    Returns (O rounded [B,Hq,N,d] f32 values, O before the final rounding
+    [B,Hq,N,d] f32, lse [B,Hq,N] f64). ``blocks`` restricts the work to a list
+    of (b, hq, i); other entries are NaN.
+    """
+    vdt = None
+    try:
+        import torch
+        if isinstance(v, torch.Tensor):
+            vdt = {torch.bfloat16: "bf16", torch.float16: "f16"}.get(v.dtype)
+    except ImportError:  # pragma: no cover
+        pass
+    p_dtype = p_dtype or vdt
+    out_dtype = out_dtype or vdt
+    if p_dtype is None or out_dtype is None:
+        raise ValueError("p_dtype/out_dtype needed when V is not a 16-bit torch tensor")
+    v64 = _as_f64(v)
+    B, _, N, d = q_i8.shape
+    group = Hq // Hkv
+    sparse = kv_idx is not None
+    if sparse and kv_tile != K_BLOCK:
+        raise ValueError("the sparse path iterates 64-key blocks")
+    if N % kv_tile or kv_tile % K_BLOCK:
+        raise ValueError("kv_tile must be a multiple of 64 dividing N")
+    c = softmax_scale_log2(d)
+    nqb = N // Q_BLOCK
+    O = np.full((B, Hq, N, d), np.nan, dtype=np.float32)
+    O_pre = np.full((B, Hq, N, d), np.nan, dtype=np.float32)
+    lse = np.full((B, Hq, N), np.nan)
+    if blocks is None:
+        blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nqb)]
+    ninf = np.float32(-np.inf)
+    for b, hq, i in blocks:
+        hk = hq // group
+        r0 = i * Q_BLOCK
+        rows = np.arange(r0, r0 + Q_BLOCK)
+        qc = q_i8[b, hq, r0:r0 + Q_BLOCK].astype(np.float64)
+        alpha_q = np.float32(np.float32(q_scale[b, hq, i]) * c)
+        m = np.full(Q_BLOCK, ninf, dtype=np.float32)
+        l = np.zeros(Q_BLOCK)
+        acc = np.zeros((Q_BLOCK, d))
+        if sparse:
+            tiles = [int(j) for j in kv_idx[b, hq, i, :kv_cnt[b, hq, i]]]
+        else:
+            tiles = _kv_tiles_dense(i, N, causal, kv_tile)
+        for t in tiles:
+            k0 = t * kv_tile
+            keys = np.arange(k0, k0 + kv_tile)
+            # INT8 Q K^T: exact integers (|S| <= d * 127^2 < 2^53)
+            S = qc @ k_i8[b, hk, k0:k0 + kv_tile].astype(np.float64).T
+            kb = keys // K_BLOCK
+            alpha = (alpha_q * np.asarray(k_scale[b, hk, kb], dtype=np.float32)).astype(np.float32)
+            s = (S.astype(np.float32) * alpha[None, :]).astype(np.float32)
+            if causal:
+                s = np.where(keys[None, :] <= rows[:, None], s, ninf)
+            m_new = np.maximum(m, s.max(axis=1))
+            live = np.isfinite(m_new)
+            arg = np.where(live[:, None], (s - np.where(live, m_new, 0)[:, None]).astype(np.float32), ninf)
+            P = np.exp2(arg.astype(np.float64)).astype(np.float32)
+            P_hat = round_to_dtype(P, p_dtype).astype(np.float64)
+            dm = np.where(np.isfinite(m), (m - np.where(live, m_new, 0)).astype(np.float32), ninf)
+            corr = np.where(np.isfinite(m), np.exp2(dm.astype(np.float64)).astype(np.float32), 0.0)
+            corr = np.where(live, corr, 1.0).astype(np.float64)
+            l = l * corr + P_hat.sum(axis=1)
+            acc = acc * corr[:, None] + P_hat @ v64[b, hk, k0:k0 + kv_tile]
+            m = m_new
+        with np.errstate(invalid="ignore", divide="ignore"):
+            o32 = np.where(l[:, None] > 0, acc / l[:, None], 0.0).astype(np.float32)
+            lse[b, hq, r0:r0 + Q_BLOCK] = np.where(
+                l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(l)), -np.inf)
+        O_pre[b, hq, r0:r0 + Q_BLOCK] = o32
+        O[b, hq, r0:r0 + Q_BLOCK] = round_to_dtype(o32, out_dtype)
+    return O, O_pre, lse
