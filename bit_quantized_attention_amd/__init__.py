@@ -1,0 +1,253 @@
+"""Python binding of libqattn (8-bit quantized, optionally block-sparse attention
+forward for MI355X / gfx950).
+
+The functions ``qattn_smooth_quant``, ``qattn_block_mask``, ``qattn_fwd`` and the
+size helpers carry the names of the C entry points declared in
+``include/qattn.h`` and only marshal arguments: torch tensors supply device
+memory, torch's current HIP stream supplies the stream, and every step of the
+computation runs in the library's HIP kernels. There is no fallback: if the
+shared library is not built, ``load()`` raises.
+
+``attention(q, k, v, causal, sparse)`` chains the three calls with freshly
+allocated intermediates; ``Plan`` does the same with intermediates allocated once
+(for repeated calls on one shape).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqattn.so")
+
+QATTN_F16 = 0
+QATTN_BF16 = 1
+Q_BLOCK = 128
+K_BLOCK = 64
+KV_TILE = 64
+
+_STATUS = {0: "QATTN_OK", 1: "QATTN_ERR_NULL", 2: "QATTN_ERR_SHAPE", 3: "QATTN_ERR_ALIGN",
+           4: "QATTN_ERR_UNSUPPORTED", 5: "QATTN_ERR_ARG", 6: "QATTN_ERR_DEVICE"}
+
+_lib = None
+
+
+class QattnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = qattn_status_str(status) if _lib is not None else ""
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({msg})")
+
+
+class qattn_problem_t(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32)]
+
+
+def load(path: str = LIB_PATH):
+    """Load libqattn.so (once). Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m bit_quantized_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER(qattn_problem_t)
+    lib.qattn_status_str.argtypes = [ctypes.c_int]
+    lib.qattn_status_str.restype = ctypes.c_char_p
+    lib.qattn_version.argtypes = []
+    lib.qattn_version.restype = ctypes.c_char_p
+    lib.qattn_workspace_bytes.argtypes = [P]
+    lib.qattn_workspace_bytes.restype = sz
+    lib.qattn_max_keep.argtypes = [P, i32, i32]
+    lib.qattn_max_keep.restype = i32
+    lib.qattn_smooth_quant.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.qattn_smooth_quant.restype = ctypes.c_int
+    lib.qattn_block_mask.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.qattn_block_mask.restype = ctypes.c_int
+    lib.qattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.qattn_fwd.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---- marshalling helpers -------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (None -> NULL); ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QattnError(status, where)
+
+
+def problem(B: int, Hq: int, Hkv: int, N: int, d: int, dtype, causal: bool) -> qattn_problem_t:
+    """Build a qattn_problem_t; dtype is "f16"/"bf16", a torch dtype, or 0/1."""
+    if not isinstance(dtype, int):
+        name = str(dtype)
+        if "bfloat16" in name or name == "bf16":
+            dtype = QATTN_BF16
+        elif "float16" in name or name == "f16":
+            dtype = QATTN_F16
+        else:
+            raise ValueError(f"unsupported dtype {dtype}")
+    return qattn_problem_t(B, Hq, Hkv, N, d, dtype, int(bool(causal)) if causal in (0, 1, True, False) else causal)
+
+
+def problem_of(q, k, causal: bool) -> qattn_problem_t:
+    B, Hq, N, d = q.shape
+    return problem(B, Hq, k.shape[1], N, d, q.dtype, causal)
+
+
+# ---- the C entry points ----------------------------------------------------------
+
+def qattn_status_str(status: int) -> str:
+    return load().qattn_status_str(status).decode()
+
+
+def qattn_version() -> str:
+    return load().qattn_version().decode()
+
+
+def qattn_workspace_bytes(p: qattn_problem_t) -> int:
+    return load().qattn_workspace_bytes(ctypes.byref(p))
+
+
+def qattn_max_keep(p: qattn_problem_t, keep_num: int, keep_den: int) -> int:
+    return load().qattn_max_keep(ctypes.byref(p), keep_num, keep_den)
+
+
+def qattn_smooth_quant(p, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool,
+                       workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load().qattn_smooth_quant(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(q_i8), _ptr(q_scale),
+                                   _ptr(k_i8), _ptr(k_scale), _ptr(k_mean), _ptr(q_pool),
+                                   _ptr(k_pool), _ptr(workspace), workspace_bytes,
+                                   _stream(stream))
+    if check:
+        _check(st, "qattn_smooth_quant")
+    return st
+
+
+def qattn_block_mask(p, q_pool, k_pool, keep_num, keep_den, max_keep, kv_idx, kv_cnt,
+                     workspace, workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load().qattn_block_mask(ctypes.byref(p), _ptr(q_pool), _ptr(k_pool), keep_num, keep_den,
+                                 max_keep, _ptr(kv_idx), _ptr(kv_cnt), _ptr(workspace),
+                                 workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "qattn_block_mask")
+    return st
+
+
+def qattn_fwd(p, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt, max_keep, o, lse=None,
+              stream=None, check=True) -> int:
+    st = load().qattn_fwd(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_i8), _ptr(k_scale),
+                          _ptr(v), _ptr(kv_idx), _ptr(kv_cnt), max_keep, _ptr(o), _ptr(lse),
+                          _stream(stream))
+    if check:
+        _check(st, "qattn_fwd")
+    return st
+
+
+# ---- convenience: allocate intermediates and chain the calls ----------------------
+
+@dataclass
+class Plan:
+    """Intermediates for one problem shape, allocated once on ``device``.
+
+    ``sparse`` is None (dense) or a keep ratio (keep_num, keep_den).
+    """
+
+    p: qattn_problem_t
+    device: object
+    sparse: Optional[Tuple[int, int]] = None
+    with_lse: bool = False
+    pools: Optional[bool] = None  # pooled block means; default: only when sparse
+
+    def __post_init__(self):
+        import torch
+        p, dev = self.p, self.device
+        B, Hq, Hkv, N, d = p.B, p.Hq, p.Hkv, p.N, p.d
+        nqb, nkb = N // Q_BLOCK, N // K_BLOCK
+        e = dict(device=dev)
+        self.q_i8 = torch.empty((B, Hq, N, d), dtype=torch.int8, **e)
+        self.q_scale = torch.empty((B, Hq, nqb), dtype=torch.float32, **e)
+        self.k_i8 = torch.empty((B, Hkv, N, d), dtype=torch.int8, **e)
+        self.k_scale = torch.empty((B, Hkv, nkb), dtype=torch.float32, **e)
+        self.k_mean = torch.empty((B, Hkv, d), dtype=torch.float32, **e)
+        self.workspace = torch.empty(max(16, qattn_workspace_bytes(p)), dtype=torch.uint8, **e)
+        self.q_pool = self.k_pool = self.kv_idx = self.kv_cnt = None
+        self.max_keep = 0
+        if self.pools or (self.pools is None and self.sparse is not None):
+            self.q_pool = torch.empty((B, Hq, nqb, d), dtype=torch.float32, **e)
+            self.k_pool = torch.empty((B, Hkv, nkb, d), dtype=torch.float32, **e)
+        if self.sparse is not None:
+            if self.q_pool is None:
+                raise ValueError("a sparse plan needs the pooled block means")
+            num, den = self.sparse
+            self.max_keep = qattn_max_keep(p, num, den)
+            if self.max_keep < 0:
+                raise ValueError(f"invalid keep ratio {self.sparse}")
+            self.kv_idx = torch.empty((B, Hq, nqb, self.max_keep), dtype=torch.int32, **e)
+            self.kv_cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, **e)
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, **e) if self.with_lse else None
+
+    def smooth_quant(self, q, k, stream=None):
+        qattn_smooth_quant(self.p, q, k, self.q_i8, self.q_scale, self.k_i8, self.k_scale,
+                           self.k_mean, self.q_pool, self.k_pool, self.workspace, stream=stream)
+
+    def block_mask(self, stream=None):
+        num, den = self.sparse
+        qattn_block_mask(self.p, self.q_pool, self.k_pool, num, den, self.max_keep, self.kv_idx,
+                         self.kv_cnt, self.workspace, stream=stream)
+
+    def fwd(self, v, o, stream=None):
+        qattn_fwd(self.p, self.q_i8, self.q_scale, self.k_i8, self.k_scale, v, self.kv_idx,
+                  self.kv_cnt, self.max_keep, o, self.lse, stream=stream)
+
+    def run(self, q, k, v, o, stream=None):
+        """The whole path: smooth + quantize, [block mask], attention."""
+        self.smooth_quant(q, k, stream)
+        if self.sparse is not None:
+            self.block_mask(stream)
+        self.fwd(v, o, stream)
+        return o
+
+
+def attention(q, k, v, causal: bool = False, sparse: Optional[Tuple[int, int]] = None,
+              return_plan: bool = False, with_lse: bool = False):
+    """O = attention(Q, K, V) through the quantized path; Q [B,Hq,N,d], K/V [B,Hkv,N,d]."""
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    plan = Plan(problem_of(q, k, causal), q.device, sparse, with_lse)
+    o = torch.empty_like(q)
+    plan.run(q, k, v, o)
+    return (o, plan) if return_plan else o

@@ -1,0 +1,139 @@
+// C ABI of the qattn library: host-side validation, then the kernel launchers.
+// Every check happens before the first HIP call; no exception leaves this file.
+#include "../../include/qattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "qattn_internal.h"
+
+namespace {
+
+using qattn::Shape;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+qattn_status_t check_problem(const qattn_problem_t* p, Shape* s) {
+  if (p == nullptr) return QATTN_ERR_NULL;
+  if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->N <= 0 || p->d <= 0) return QATTN_ERR_SHAPE;
+  if (p->Hq % p->Hkv != 0) return QATTN_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return QATTN_ERR_UNSUPPORTED;
+  if (p->N % QATTN_Q_BLOCK != 0) return QATTN_ERR_UNSUPPORTED;
+  if (p->dtype != QATTN_F16 && p->dtype != QATTN_BF16) return QATTN_ERR_UNSUPPORTED;
+  if (p->causal != 0 && p->causal != 1) return QATTN_ERR_ARG;
+  // element offsets and token indices stay within the integer types used in
+  // the kernels (64-bit element offsets, 32-bit tokens and block indices)
+  const long long rows = (long long)p->B * p->Hq * p->N;
+  if (rows > (1LL << 40)) return QATTN_ERR_UNSUPPORTED;
+  s->B = p->B;
+  s->Hq = p->Hq;
+  s->Hkv = p->Hkv;
+  s->N = p->N;
+  s->d = p->d;
+  s->bf16 = p->dtype == QATTN_BF16 ? 1 : 0;
+  s->causal = p->causal;
+  return QATTN_OK;
+}
+
+bool ratio_ok(int32_t num, int32_t den) { return den > 0 && num >= 0 && num <= den; }
+
+int32_t max_keep_of(const Shape& s, int32_t num, int32_t den) {
+  const long long nkb = s.nkb();
+  long long k = 3 + (nkb * num + den - 1) / den;
+  if (k > nkb) k = nkb;
+  return (int32_t)k;
+}
+
+qattn_status_t launched(hipError_t e) { return e == hipSuccess ? QATTN_OK : QATTN_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qattn_status_str(qattn_status_t status) {
+  switch (status) {
+    case QATTN_OK: return "ok";
+    case QATTN_ERR_NULL: return "a required pointer is NULL";
+    case QATTN_ERR_SHAPE: return "invalid shape (a dimension <= 0, or Hq not a multiple of Hkv)";
+    case QATTN_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case QATTN_ERR_UNSUPPORTED:
+      return "unsupported problem (d must be 64 or 128, N a multiple of 128, dtype f16/bf16)";
+    case QATTN_ERR_ARG: return "invalid argument (flag, keep ratio, max_keep or workspace size)";
+    case QATTN_ERR_DEVICE: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* qattn_version(void) { return "qattn 0.1.0 gfx950"; }
+
+size_t qattn_workspace_bytes(const qattn_problem_t* p) {
+  Shape s;
+  if (check_problem(p, &s) != QATTN_OK) return 0;
+  const size_t a = qattn::ksum_workspace_bytes(s);
+  const size_t b = qattn::mask_workspace_bytes(s);
+  return a > b ? a : b;
+}
+
+int32_t qattn_max_keep(const qattn_problem_t* p, int32_t keep_num, int32_t keep_den) {
+  Shape s;
+  if (check_problem(p, &s) != QATTN_OK || !ratio_ok(keep_num, keep_den)) return -1;
+  return max_keep_of(s, keep_num, keep_den);
+}
+
+qattn_status_t qattn_smooth_quant(const qattn_problem_t* p, const void* q, const void* k,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8, float* k_scale,
+                                  float* k_mean, float* q_pool, float* k_pool, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean || !workspace)
+    return QATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool, workspace};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (workspace_bytes < qattn::ksum_workspace_bytes(s)) return QATTN_ERR_ARG;
+  return launched(qattn::launch_smooth_quant(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool,
+                                             k_pool, workspace,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool, const float* k_pool,
+                                int32_t keep_num, int32_t keep_den, int32_t max_keep,
+                                int32_t* kv_idx, int32_t* kv_cnt, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.nkb() > qattn::mask_max_nkb()) return QATTN_ERR_UNSUPPORTED;
+  if (!q_pool || !k_pool || !kv_idx || !kv_cnt || !workspace) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_pool, k_pool, kv_idx, kv_cnt, workspace};
+  for (const void* x : ptrs)
+    if (misaligned(x)) return QATTN_ERR_ALIGN;
+  if (!ratio_ok(keep_num, keep_den)) return QATTN_ERR_ARG;
+  if (max_keep < max_keep_of(s, keep_num, keep_den)) return QATTN_ERR_ARG;
+  if (workspace_bytes < qattn::mask_workspace_bytes(s)) return QATTN_ERR_ARG;
+  return launched(qattn::launch_block_mask(s, q_pool, k_pool, keep_num, keep_den, max_keep, kv_idx,
+                                           kv_cnt, workspace, static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const float* q_scale,
+                         const int8_t* k_i8, const float* k_scale, const void* v,
+                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_keep, void* o,
+                         float* lse, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !o) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_i8, q_scale, k_i8, k_scale, v, o, lse, kv_idx, kv_cnt};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return QATTN_ERR_ARG;
+  if (kv_idx != nullptr && max_keep < 1) return QATTN_ERR_ARG;
+  return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
+                                         max_keep, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

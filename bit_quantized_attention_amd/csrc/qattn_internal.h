@@ -1,0 +1,47 @@
+// Internal declarations shared by the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qattn {
+
+constexpr int kQBlock = 128;     // query tokens per quantization block
+constexpr int kKBlock = 64;      // key tokens per quantization block
+constexpr int kKsumChunk = 512;  // tokens per partial K sum
+
+struct Shape {
+  int B, Hq, Hkv, N, d;
+  int bf16;    // 1: bfloat16, 0: float16
+  int causal;  // 0/1
+  int nqb() const { return N / kQBlock; }
+  int nkb() const { return N / kKBlock; }
+  int nchunk() const { return (N + kKsumChunk - 1) / kKsumChunk; }
+};
+
+// Bytes of exact partial sums that launch_smooth_quant needs.
+inline size_t ksum_workspace_bytes(const Shape& s) {
+  return (size_t)s.B * s.Hkv * s.nchunk() * s.d * 2 * sizeof(double);
+}
+
+hipError_t launch_smooth_quant(const Shape& s, const void* q, const void* k, int8_t* q_i8,
+                               float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                               float* q_pool, float* k_pool, void* workspace,
+                               hipStream_t stream);
+
+// Bytes of pooled-vector INT8 codes and scales that launch_block_mask needs.
+size_t mask_workspace_bytes(const Shape& s);
+// Largest N/64 the block mask supports.
+int mask_max_nkb();
+
+hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k_pool,
+                             int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
+                             int32_t* kv_cnt, void* workspace, hipStream_t stream);
+
+hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
+                           const int8_t* k_i8, const float* k_scale, const void* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
+                           void* o, float* lse, hipStream_t stream);
+
+}  // namespace qattn

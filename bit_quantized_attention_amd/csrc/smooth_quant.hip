@@ -1,0 +1,236 @@
+// K smoothing and per-block INT8 quantization of Q and K (bandwidth-bound).
+//
+// Three launches on the caller's stream:
+//   1. ksum_partial   -- exact per-channel sums of K over 512-token chunks
+//                        (fp64 double-double), one workgroup per (chunk, b*hk);
+//   2. kmean_finalize -- merge the chunks, k_mean = fl32(fl64(sum) / N);
+//   3. quant          -- one workgroup per Q block (128 tokens) or K block
+//                        (64 tokens): amax, scale, exact RNE codes, optional
+//                        pooled block means.
+// Every element is read with 16-byte vector loads; a 64-lane wave covers 4
+// (d = 128) or 8 (d = 64) contiguous rows per load instruction.
+#include "device_util.h"
+#include "qattn_internal.h"
+
+// The rounding sequence of every value here is fixed by the definition: no
+// contraction of a*b+c into fma anywhere in this file.
+#pragma clang fp contract(off)
+
+namespace qattn {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void ksum_partial_kernel(const uint16_t* __restrict__ k,
+                                                                double2* __restrict__ part,
+                                                                int N, int nchunk) {
+  constexpr int LPR = D / 8;          // lanes per row (16 bytes each)
+  constexpr int RPI = kThreads / LPR; // rows per iteration
+  __shared__ double2 red[RPI][D];
+  const int chunk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int cg = threadIdx.x % LPR;
+  const int rg = threadIdx.x / LPR;
+  const int t0 = chunk * kKsumChunk;
+  const int t1 = min(N, t0 + kKsumChunk);
+  const uint16_t* base = k + (size_t)bh * N * D + cg * 8;
+  double hi[8], lo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hi[e] = lo[e] = 0.0;
+  for (int t = t0 + rg; t < t1; t += RPI) {
+    float x[8];
+    load8_f32<BF16>(base + (size_t)t * D, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd_add(hi[e], lo[e], (double)x[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = make_double2(hi[e], lo[e]);
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    double H = 0.0, L = 0.0;
+    for (int r = 0; r < RPI; ++r) dd_merge(H, L, red[r][c].x, red[r][c].y);
+    part[((size_t)bh * nchunk + chunk) * D + c] = make_double2(H, L);
+  }
+}
+
+__global__ __launch_bounds__(128) void kmean_finalize_kernel(const double2* __restrict__ part,
+                                                             float* __restrict__ k_mean,
+                                                             int N, int nchunk, int D) {
+  const int bh = blockIdx.x;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    double H = 0.0, L = 0.0;
+    for (int ch = 0; ch < nchunk; ++ch) {
+      const double2 v = part[((size_t)bh * nchunk + ch) * D + c];
+      dd_merge(H, L, v.x, v.y);
+    }
+    const double s = H + L;  // the fp64 value nearest the exact sum
+    k_mean[(size_t)bh * D + c] = (float)(s / (double)N);
+  }
+}
+
+struct QuantArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* k_mean;
+  int8_t* q_i8;
+  float* q_scale;
+  int8_t* k_i8;
+  float* k_scale;
+  float* q_pool;
+  float* k_pool;
+  int N;
+  int nQ;   // number of Q blocks = B*Hq*nqb
+  int nqb;
+  int nkb;
+};
+
+// One block of ROWS tokens x D channels: src/dst point at its first row.
+template <int D, bool BF16, int ROWS, bool IS_K>
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src,
+                                            const float* __restrict__ mean,
+                                            int8_t* __restrict__ dst, float* scale_out,
+                                            float* __restrict__ pool_out,
+                                            double2 (*red)[D], float* wmax) {
+  constexpr int LPR = D / 8;
+  constexpr int RPI = kThreads / LPR;
+  constexpr int RPT = ROWS / RPI;  // rows per thread
+  const int cg = threadIdx.x % LPR;
+  const int rg = threadIdx.x / LPR;
+  float x[RPT][8];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) load8_f32<BF16>(src + (size_t)(rg + i * RPI) * D + cg * 8, x[i]);
+
+  if (pool_out != nullptr) {
+    // exact column sums of the raw 16-bit values
+    double hi[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hi[e] = lo[e] = 0.0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dd_add(hi[e], lo[e], (double)x[i][e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = make_double2(hi[e], lo[e]);
+  }
+
+  float m[8];
+  if constexpr (IS_K) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = mean[cg * 8 + e];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] - m[e];
+  }
+
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i][e]));
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+  const float scale = quant_scale(amax);
+  const float inv = 1.0f / scale;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    uint2 w;
+    w.x = pack4_i8(quant_code(x[i][0], scale, inv), quant_code(x[i][1], scale, inv),
+                   quant_code(x[i][2], scale, inv), quant_code(x[i][3], scale, inv));
+    w.y = pack4_i8(quant_code(x[i][4], scale, inv), quant_code(x[i][5], scale, inv),
+                   quant_code(x[i][6], scale, inv), quant_code(x[i][7], scale, inv));
+    *reinterpret_cast<uint2*>(dst + (size_t)(rg + i * RPI) * D + cg * 8) = w;
+  }
+  if (threadIdx.x == 0) *scale_out = scale;
+
+  if (pool_out != nullptr && threadIdx.x < D) {
+    const int c = threadIdx.x;
+    double H = 0.0, L = 0.0;
+    for (int r = 0; r < RPI; ++r) dd_merge(H, L, red[r][c].x, red[r][c].y);
+    const double s = H + L;
+    if constexpr (IS_K) {
+      pool_out[c] = (float)(s / (double)ROWS - (double)mean[c]);
+    } else {
+      pool_out[c] = (float)(s / (double)ROWS);
+    }
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
+  constexpr int RPI = kThreads / (D / 8);
+  __shared__ double2 red[RPI][D];
+  __shared__ float wmax[kThreads / 64];
+  const int blk = blockIdx.x;
+  if (blk < a.nQ) {
+    const size_t bh = blk / a.nqb;  // b * Hq + hq
+    const int i = blk % a.nqb;
+    const size_t row0 = bh * a.N + (size_t)i * kQBlock;
+    quant_block<D, BF16, kQBlock, false>(a.q + row0 * D, nullptr, a.q_i8 + row0 * D,
+                                         a.q_scale + blk,
+                                         a.q_pool ? a.q_pool + (size_t)blk * D : nullptr, red,
+                                         wmax);
+  } else {
+    const int kblk = blk - a.nQ;
+    const size_t bh = kblk / a.nkb;  // b * Hkv + hk
+    const int j = kblk % a.nkb;
+    const size_t row0 = bh * a.N + (size_t)j * kKBlock;
+    quant_block<D, BF16, kKBlock, true>(a.k + row0 * D, a.k_mean + bh * D, a.k_i8 + row0 * D,
+                                        a.k_scale + kblk,
+                                        a.k_pool ? a.k_pool + (size_t)kblk * D : nullptr, red,
+                                        wmax);
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch(const Shape& s, const void* q, const void* k, int8_t* q_i8, float* q_scale,
+                  int8_t* k_i8, float* k_scale, float* k_mean, float* q_pool, float* k_pool,
+                  void* workspace, hipStream_t stream) {
+  const int nchunk = s.nchunk();
+  double2* part = static_cast<double2*>(workspace);
+  hipLaunchKernelGGL((ksum_partial_kernel<D, BF16>), dim3(nchunk, s.B * s.Hkv), dim3(kThreads), 0,
+                     stream, static_cast<const uint16_t*>(k), part, s.N, nchunk);
+  hipLaunchKernelGGL(kmean_finalize_kernel, dim3(s.B * s.Hkv), dim3(128), 0, stream, part, k_mean,
+                     s.N, nchunk, D);
+  QuantArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.k_mean = k_mean;
+  a.q_i8 = q_i8;
+  a.q_scale = q_scale;
+  a.k_i8 = k_i8;
+  a.k_scale = k_scale;
+  a.q_pool = q_pool;
+  a.k_pool = k_pool;
+  a.N = s.N;
+  a.nqb = s.nqb();
+  a.nkb = s.nkb();
+  a.nQ = s.B * s.Hq * a.nqb;
+  const int nK = s.B * s.Hkv * a.nkb;
+  hipLaunchKernelGGL((quant_kernel<D, BF16>), dim3(a.nQ + nK), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_smooth_quant(const Shape& s, const void* q, const void* k, int8_t* q_i8,
+                               float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,
+                               float* q_pool, float* k_pool, void* workspace,
+                               hipStream_t stream) {
+  if (s.d == 128) {
+    return s.bf16 ? launch<128, true>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool,
+                                      k_pool, workspace, stream)
+                  : launch<128, false>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool,
+                                       k_pool, workspace, stream);
+  }
+  return s.bf16 ? launch<64, true>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool,
+                                   workspace, stream)
+                : launch<64, false>(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool,
+                                    workspace, stream);
+}
+
+}  // namespace qattn

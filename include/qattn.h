@@ -1,0 +1,192 @@
+/*
+ * qattn -- 8-bit quantized, optionally block-sparse attention forward (prefill)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are explainer pages; each entry point below cites the
+ * passage that defines its operation):
+ *   1. smooth K by subtracting its per-channel mean over tokens, and quantize
+ *      Q (128-token blocks) and smoothed K (64-token blocks) to INT8 with one
+ *      fp32 scale per block;
+ *   2. optionally score every (query block, key block) pair by the dot product
+ *      of their INT8-quantized mean vectors and keep, per query block, the
+ *      first block, the diagonal blocks and the top fraction of the rest;
+ *   3. compute S = Q K^T on INT8 matrix cores, an online base-2 softmax, and
+ *      P V on FP16/BF16 matrix cores with FP32 accumulation, visiting only the
+ *      kept key blocks when a mask is given.
+ *
+ * Conventions shared by every entry point:
+ *   - Layouts are contiguous row-major: Q and O are [B, Hq, N, d]; K and V are
+ *     [B, Hkv, N, d]. Query head hq reads kv head hq / (Hq / Hkv).
+ *   - Causal masking is top-left aligned: key j is visible to query i iff
+ *     j <= i.
+ *   - Every tensor pointer is a device pointer owned by the caller and must be
+ *     16-byte aligned. The library allocates and frees nothing and keeps no
+ *     mutable state; calls on different streams may run concurrently.
+ *   - `stream` is a hipStream_t passed as void* (NULL: the default stream).
+ *     Work is enqueued on it; no call synchronizes.
+ *   - Arguments are validated on the host before any HIP call. A failing
+ *     validation returns its status and enqueues nothing. A launch failure
+ *     returns QATTN_ERR_DEVICE. No C++ exception crosses this interface.
+ *   - Supported: d in {64, 128}; N a positive multiple of 128; dtype f16 or
+ *     bf16 for Q, K, V and O.
+ */
+#ifndef QATTN_H
+#define QATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QATTN_OK = 0,
+  QATTN_ERR_NULL = 1,        /* a required pointer is NULL                  */
+  QATTN_ERR_SHAPE = 2,       /* a dimension <= 0, or Hq % Hkv != 0          */
+  QATTN_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned     */
+  QATTN_ERR_UNSUPPORTED = 4, /* d not 64/128, N % 128 != 0, unknown dtype   */
+  QATTN_ERR_ARG = 5,         /* bad flag, keep ratio, max_keep or workspace */
+  QATTN_ERR_DEVICE = 6       /* a HIP launch reported an error              */
+} qattn_status_t;
+
+typedef enum { QATTN_F16 = 0, QATTN_BF16 = 1 } qattn_dtype_t;
+
+typedef struct {
+  int32_t B;      /* batch                                  */
+  int32_t Hq;     /* query heads                            */
+  int32_t Hkv;    /* key/value heads, divides Hq            */
+  int32_t N;      /* tokens (queries = keys)                */
+  int32_t d;      /* head dimension                         */
+  int32_t dtype;  /* qattn_dtype_t of Q, K, V and O         */
+  int32_t causal; /* 0 or 1                                 */
+} qattn_problem_t;
+
+/* Quantization block lengths (tokens) and the key tile of the online softmax. */
+#define QATTN_Q_BLOCK 128
+#define QATTN_K_BLOCK 64
+#define QATTN_KV_TILE 64
+
+/* Message for a status code (static storage, never NULL). */
+const char* qattn_status_str(qattn_status_t status);
+
+/* Library version string. */
+const char* qattn_version(void);
+
+/* Device workspace bytes that qattn_smooth_quant (per-chunk exact partial
+ * sums of K) and qattn_block_mask (INT8 codes and scales of the pooled
+ * vectors) need for `p`; one buffer of this size serves both calls when they
+ * run in stream order. 0 when `p` is NULL or invalid. */
+size_t qattn_workspace_bytes(const qattn_problem_t* p);
+
+/* Length of each kept list that qattn_block_mask writes for a keep ratio of
+ * keep_num / keep_den: min(N/64, 3 + ceil((N/64) * keep_num / keep_den)).
+ * Returns -1 for an invalid problem or ratio. */
+int32_t qattn_max_keep(const qattn_problem_t* p, int32_t keep_num, int32_t keep_den);
+
+/*
+ * qattn_smooth_quant -- K smoothing and per-block INT8 quantization.
+ *
+ * Defined by the SageAttention explainer (aibr.jp/archives/102657), sections 2
+ * and 3: K is smoothed so that extreme per-channel values do not inflate the
+ * quantization scale, and the attention inputs are quantized to 8 bits. The
+ * pages give no formulas; this library computes:
+ *   k_mean[b,hk,c] = fl32(fl64(fl64(exact sum over t of K[b,hk,t,c]) / N))
+ *   Ks             = fl32(fl32(K) - k_mean)            (per channel)
+ *   per block X (Q: 128 tokens x d of one (b, hq); Ks: 64 tokens x d):
+ *     scale = fl32(amax|X| / 127), or 1.0 when that is 0;
+ *     code  = clamp(round-half-even(x / scale), -127, 127), x / scale exact.
+ *   optional pooled block means (inputs of qattn_block_mask):
+ *     q_pool[b,hq,i,c] = fl32(fl64(exact sum over the 128 tokens of Q) / 128)
+ *     k_pool[b,hk,j,c] = fl32(fl64(fl64(exact sum over the 64 tokens of K) / 64)
+ *                             - k_mean[b,hk,c])
+ *   The sums are exact (hence independent of reduction order) whenever, per
+ *   channel, max|K| / (smallest nonzero |K|) < 2^64 -- always for f16.
+ *
+ * In:  q [B,Hq,N,d], k [B,Hkv,N,d] in p->dtype.
+ * Out: q_i8 [B,Hq,N,d] int8, q_scale [B,Hq,N/128] f32,
+ *      k_i8 [B,Hkv,N,d] int8, k_scale [B,Hkv,N/64] f32, k_mean [B,Hkv,d] f32,
+ *      q_pool [B,Hq,N/128,d] f32 and k_pool [B,Hkv,N/64,d] f32 (each may be
+ *      NULL: not computed).
+ * workspace: device scratch of at least qattn_workspace_bytes(p) bytes,
+ *      overwritten; it must not be shared with a concurrent call.
+ * Errors: NULL for a missing required pointer; SHAPE/UNSUPPORTED for the
+ *      problem; ALIGN; ARG when workspace_bytes is too small or causal is not
+ *      0/1; DEVICE on launch failure.
+ */
+qattn_status_t qattn_smooth_quant(const qattn_problem_t* p, const void* q, const void* k,
+                                  int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                                  float* k_scale, float* k_mean, float* q_pool,
+                                  float* k_pool, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * qattn_block_mask -- per query block, the key blocks to keep.
+ *
+ * Score: the ThriftAttention summary (gist.science/ja/paper/2605.23081),
+ * technical summary, method (heuristic block selection): a (query block i,
+ * key block j) pair is scored by the dot product of the blocks' mean vectors
+ * and the top-k pairs are selected. Skipping the rest while keeping the first
+ * (sink) and diagonal (local) blocks: the SALE explainer
+ * (aibr.jp/archives/118208), section 3. This library computes, per
+ * (b, hq, i) with hk = hq / (Hq/Hkv):
+ *   each pooled vector is INT8-quantized on its own (the rule above, over its
+ *   d channels); dot = exact integer dot product of the codes;
+ *   score[i,j] = fl32(fl32(float(dot) * q_scale_i) * k_scale_j);
+ *   valid = { j : 64 j <= 128 i + 127 } if causal, else all j < N/64;
+ *   forced = valid & { 0, 2i, 2i+1 };
+ *   kcount = ceil(|valid| * keep_num / keep_den) (integer arithmetic);
+ *   kept = forced + the top min(kcount, |valid \ forced|) of valid \ forced by
+ *          (score descending, j ascending).
+ * In:  q_pool [B,Hq,N/128,d], k_pool [B,Hkv,N/64,d] f32 (from qattn_smooth_quant).
+ * Out: kv_idx [B,Hq,N/128,max_keep] int32, kept blocks ascending then -1;
+ *      kv_cnt [B,Hq,N/128] int32, number of kept blocks.
+ * workspace: device scratch of at least qattn_workspace_bytes(p) bytes,
+ *      overwritten; it must not be shared with a concurrent call.
+ * Errors: NULL; SHAPE; UNSUPPORTED also when N > 131072; ALIGN; ARG when
+ *      keep_num < 0, keep_den <= 0, keep_num > keep_den,
+ *      max_keep < qattn_max_keep(p, keep_num, keep_den), or the workspace is
+ *      too small; DEVICE.
+ */
+qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool,
+                                const float* k_pool, int32_t keep_num, int32_t keep_den,
+                                int32_t max_keep, int32_t* kv_idx, int32_t* kv_cnt,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qattn_fwd -- quantized attention forward.
+ *
+ * Kernel: the SageAttention explainer (aibr.jp/archives/102657), section 3
+ * (INT8 matrix products for Q K^T, 16-bit products for P V, on the matrix
+ * units) and section 4 (FlashAttention-style tiling); online softmax merge as
+ * in the ThriftAttention summary (gist.science/ja/paper/2605.23081), technical
+ * summary, method. This library computes, per (b, hq), per query block of 128
+ * rows and per key tile of 64 keys in ascending order (all causally visible
+ * tiles when dense; the kept tiles when kv_idx is given):
+ *   S = q_codes k_codes^T (exact int32);
+ *   alpha = fl32(fl32(q_scale * fl32(log2(e)/sqrt(d))) * k_scale);
+ *   s = S * alpha, -inf where the key is masked;
+ *   m' = max(m, rowmax s); P = exp2(s - m') rounded to V's dtype;
+ *   l = l * exp2(m - m') + rowsum P; acc = acc * exp2(m - m') + P V (fp32);
+ *   O = acc / l rounded to V's dtype; lse = ln2 * (m + log2 l), the natural
+ *   log-sum-exp of the smoothed, dequantized logits (S * alpha / log2(e)).
+ * In:  q_i8, q_scale, k_i8, k_scale as written by qattn_smooth_quant;
+ *      v [B,Hkv,N,d] in p->dtype; kv_idx/kv_cnt from qattn_block_mask or NULL
+ *      for dense (both NULL, or both non-NULL with the max_keep they were
+ *      written with). Kept-list entries outside [0, N/64), entries past the
+ *      query block's causal range, and counts above max_keep are ignored.
+ * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL. A query row with
+ *      no visible key gets O = 0 and lse = -inf.
+ * Errors: NULL; SHAPE/UNSUPPORTED; ALIGN; ARG when exactly one of
+ *      kv_idx/kv_cnt is NULL or max_keep < 1 with a mask; DEVICE.
+ */
+qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const float* q_scale,
+                         const int8_t* k_i8, const float* k_scale, const void* v,
+                         const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_keep,
+                         void* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QATTN_H */

@@ -1,0 +1,83 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI, run the
+oracle on the same inputs (optionally on a slice of heads / query blocks), and
+the comparison metrics with their tolerances."""
+
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+
+# Output tolerance of the quantized path against its emulation (max-abs-relative
+# of the difference before the final 16-bit rounding, see out_err below) and the
+# cosine-similarity floor against exact fp64 attention.
+TOL_EMU = 2e-3
+COS_MIN = 0.999
+
+
+def log(msg: str):
+    print(f"[parity {time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def ulp16(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the 16-bit dtype at |x| (bf16: 8 significant bits, f16: 11)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    bits = 8 if dtype == "bf16" else 11
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14 if dtype == "f16" else 2.0 ** -126)))
+    return np.exp2(e - (bits - 1))
+
+
+def out_err(o_gpu: np.ndarray, o_emu_pre: np.ndarray, dtype: str) -> float:
+    """max_i max(0, |o_gpu - o_emu_pre| - ulp/2) / max|o_emu_pre|.
+
+    o_gpu is the kernel's 16-bit output, o_emu_pre the emulation's output before
+    its own final rounding. Removing half an output ulp removes exactly the part
+    of the difference that the final rounding alone can make; what remains is
+    bounded by the difference before rounding."""
+    d = np.abs(o_gpu.astype(np.float64) - o_emu_pre.astype(np.float64))
+    d = np.maximum(0.0, d - 0.5 * ulp16(o_emu_pre, dtype))
+    return float(d.max() / np.abs(o_emu_pre).max())
+
+
+def max_abs_rel(a: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.abs(a.astype(np.float64) - ref.astype(np.float64)).max() / np.abs(ref).max())
+
+
+def cos(a: np.ndarray, b: np.ndarray) -> float:
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.numpy()
+
+
+def run_gpu(qa, p, t, sparse=None, pools=None, with_lse=True):
+    """The whole path on cuda:0 through the C ABI; returns (plan, o) on device."""
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
+                   sparse=sparse, with_lse=with_lse, pools=pools)
+    o = torch.empty_like(q)
+    plan.run(q, k, v, o)
+    torch.cuda.synchronize()
+    return plan, o
+
+
+def head_slice(t, p, b: int, hqs):
+    """Inputs restricted to batch b, query heads hqs (all of one kv head) and that kv head."""
+    hk = hqs[0] // p.group
+    assert all(h // p.group == hk for h in hqs)
+    sub = {"q": t["q"][b:b + 1, list(hqs)].contiguous(),
+           "k": t["k"][b:b + 1, hk:hk + 1].contiguous(),
+           "v": t["v"][b:b + 1, hk:hk + 1].contiguous()}
+    return sub, hk

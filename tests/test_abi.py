@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/qattn.h declares, and rejects every invalid argument with its status
+before any HIP call (so no call here reaches the device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_quantized_attention_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qattn.h")
+
+OK, NULL, SHAPE, ALIGN, UNSUP, ARG = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qa.LIB_PATH):
+        pytest.fail("libqattn.so is not built (run python -m bit_quantized_attention_amd.build)")
+    return qa.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert {"qattn_smooth_quant", "qattn_block_mask", "qattn_fwd"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", qa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(qattn_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert len(qa.qattn_status_str(s)) > 0
+    assert qa.qattn_status_str(99) == "unknown status"
+    assert "gfx950" in qa.qattn_version()
+
+
+def _p(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, N=256, d=128, dtype=1, causal=1)
+    base.update(kw)
+    return qa.qattn_problem_t(**base)
+
+
+# aligned, non-null fake addresses: validation must fail before they are used
+A = 1 << 20
+
+
+def _sq(p, **over):
+    args = dict(q=A, k=A, q_i8=A, q_scale=A, k_i8=A, k_scale=A, k_mean=A, q_pool=None,
+                k_pool=None, workspace=A, workspace_bytes=1 << 30)
+    args.update(over)
+    return qa.qattn_smooth_quant(p, args["q"], args["k"], args["q_i8"], args["q_scale"],
+                                 args["k_i8"], args["k_scale"], args["k_mean"], args["q_pool"],
+                                 args["k_pool"], args["workspace"], args["workspace_bytes"],
+                                 stream=0, check=False)
+
+
+def _bm(p, **over):
+    args = dict(qp=A, kp=A, num=1, den=10, mk=1000, idx=A, cnt=A, ws=A, wsb=1 << 30)
+    args.update(over)
+    return qa.qattn_block_mask(p, args["qp"], args["kp"], args["num"], args["den"], args["mk"],
+                               args["idx"], args["cnt"], args["ws"], args["wsb"], stream=0,
+                               check=False)
+
+
+def _fw(p, **over):
+    args = dict(qi=A, qs=A, ki=A, kscl=A, v=A, idx=None, cnt=None, mk=0, o=A, lse=None)
+    args.update(over)
+    return qa.qattn_fwd(p, args["qi"], args["qs"], args["ki"], args["kscl"], args["v"],
+                        args["idx"], args["cnt"], args["mk"], args["o"], args["lse"], stream=0,
+                        check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _bm, _fw])
+def test_problem_validation(lib, call):
+    assert call(_p(B=0)) == SHAPE
+    assert call(_p(Hq=0)) == SHAPE
+    assert call(_p(N=-128)) == SHAPE
+    assert call(_p(Hq=6, Hkv=4)) == SHAPE
+    assert call(_p(d=96)) == UNSUP
+    assert call(_p(d=256)) == UNSUP
+    assert call(_p(N=200)) == UNSUP          # N not a multiple of 128 (a ragged tail)
+    assert call(_p(dtype=2)) == UNSUP
+    assert call(_p(causal=2)) == ARG
+
+
+def test_null_problem(lib):
+    st = lib.qattn_fwd(None, A, A, A, A, A, None, None, 0, A, None, None)
+    assert st == NULL
+    assert lib.qattn_workspace_bytes(None) == 0
+    assert lib.qattn_max_keep(None, 1, 10) == -1
+
+
+def test_smooth_quant_arguments(lib):
+    p = _p()
+    for name in ["q", "k", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "workspace"]:
+        assert _sq(p, **{name: None}) == NULL, name
+    for name in ["q", "k", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean", "workspace"]:
+        assert _sq(p, **{name: A + 8}) == ALIGN, name
+    assert _sq(p, q_pool=A + 4) == ALIGN
+    assert _sq(p, k_pool=A + 2) == ALIGN
+    need = qa.qattn_workspace_bytes(p)
+    assert need > 0
+    assert _sq(p, workspace_bytes=need - 1) == ARG
+
+
+def test_block_mask_arguments(lib):
+    p = _p(N=1024)
+    for name in ["qp", "kp", "idx", "cnt", "ws"]:
+        assert _bm(p, **{name: None}) == NULL, name
+        assert _bm(p, **{name: A + 4}) == ALIGN, name
+    assert _bm(p, num=-1) == ARG
+    assert _bm(p, den=0) == ARG
+    assert _bm(p, num=11, den=10) == ARG
+    mk = qa.qattn_max_keep(p, 1, 10)
+    assert mk == min(16, 3 + 2)
+    assert _bm(p, mk=mk - 1) == ARG
+    assert _bm(p, wsb=qa.qattn_workspace_bytes(p) - 1) == ARG
+    assert _bm(_p(N=131072 + 128)) == UNSUP
+
+
+def test_fwd_arguments(lib):
+    p = _p()
+    for name in ["qi", "qs", "ki", "kscl", "v", "o"]:
+        assert _fw(p, **{name: None}) == NULL, name
+        assert _fw(p, **{name: A + 8}) == ALIGN, name
+    assert _fw(p, lse=A + 4) == ALIGN
+    assert _fw(p, idx=A) == ARG           # kv_idx without kv_cnt
+    assert _fw(p, cnt=A) == ARG
+    assert _fw(p, idx=A, cnt=A, mk=0) == ARG
+
+
+def test_max_keep_and_workspace_sizes(lib):
+    p = _p(N=32768, Hq=32, Hkv=8)
+    assert qa.qattn_max_keep(p, 1, 10) == 55
+    assert qa.qattn_max_keep(p, 1, 1) == 512
+    assert qa.qattn_max_keep(p, 0, 1) == 3
+    assert qa.qattn_max_keep(p, 2, 1) == -1
+    ws = qa.qattn_workspace_bytes(p)
+    # K partial sums: 8 heads x 64 chunks x 128 channels x 16 bytes; mask codes:
+    # (32*256 + 8*512) pooled vectors x (128 + 4) bytes
+    assert ws == max(8 * 64 * 128 * 16, (32 * 256 + 8 * 512) * 132)
+
+
+def test_binding_has_the_c_names():
+    for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_workspace_bytes",
+              "qattn_max_keep", "qattn_status_str", "qattn_version"]:
+        assert callable(getattr(qa, n))
+
+
+def test_load_fails_loudly_without_library(tmp_path):
+    saved = qa._lib
+    try:
+        qa._lib = None
+        with pytest.raises(ImportError):
+            qa.load(str(tmp_path / "missing.so"))
+    finally:
+        qa._lib = saved

@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: smoothing/quantization outputs (codes, scales, channel means, pooled
+means) and the block mask are bit-exact (mask rows at a near-tie excepted); the
+attention output is within TOL_EMU of the quantized-path emulation (before the
+final 16-bit rounding, see parity_util.out_err) and has cosine >= COS_MIN
+against exact fp64 attention (under the same block mask when sparse).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synthetic import make_case, make_config
+from parity_util import (TOL_EMU, COS_MIN, log, out_err, max_abs_rel, cos, to_np, run_gpu,
+                         head_slice)
+
+pytestmark = pytest.mark.gpu
+
+# (name, make_case kwargs): several 64/128-row tiles, GQA on/off, both dtypes,
+# both head sizes, N not a power of two (a partial K-sum chunk, N/128 odd)
+SMALL = [
+    ("c1", None),
+    ("bf16-d128-causal-gqa4-N1024", dict(B=1, Hq=8, Hkv=2, N=1024, d=128, dtype="bf16",
+                                         causal=True, seed=21, k_offset_std=3.0, outliers=4)),
+    ("f16-d64-nc-B2-N640", dict(B=2, Hq=4, Hkv=4, N=640, d=64, dtype="f16", causal=False,
+                                seed=22, k_offset_std=2.0)),
+    ("f16-d128-causal-gqa2-N384", dict(B=1, Hq=4, Hkv=2, N=384, d=128, dtype="f16",
+                                       causal=True, seed=23, k_offset_std=2.0)),
+    ("bf16-d64-causal-mqa-N512", dict(B=1, Hq=4, Hkv=1, N=512, d=64, dtype="bf16",
+                                      causal=True, seed=24, k_offset_std=3.0, outliers=2)),
+]
+
+
+def _case(name, kw):
+    if kw is None:
+        return make_config(1)
+    return make_case(**kw)
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_smooth_quant_bit_exact(gpu_lib, name, kw):
+    p, t = _case(name, kw)
+    log(f"smooth_quant {name}")
+    plan, _ = run_gpu(gpu_lib, p, t, pools=True)
+    ref = oracle.smooth_quant(t["q"], t["k"], pools=True)
+    for key in ["k_mean", "q_scale", "k_scale", "q_pool", "k_pool", "q_i8", "k_i8"]:
+        got = to_np(getattr(plan, key))
+        want = ref[key]
+        assert got.shape == want.shape, key
+        bad = np.count_nonzero(got != want)
+        assert bad == 0, f"{key}: {bad} of {got.size} differ"
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_fwd_matches_emulation_and_exact(gpu_lib, name, kw):
+    p, t = _case(name, kw)
+    log(f"fwd {name}")
+    plan, o = run_gpu(gpu_lib, p, t)
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    O_emu, O_pre, lse_emu = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
+                                                     sq["k_scale"], t["v"], p.causal, p.Hq, p.Hkv)
+    O_ex, _ = oracle.exact_attention(t["q"], t["k"], t["v"], p.causal)
+    og = to_np(o)
+    e = out_err(og, O_pre, p.dtype)
+    c = cos(og, O_ex)
+    log(f"  err_vs_emu={e:.3e} maxabsrel_rounded={max_abs_rel(og, O_emu):.3e} cos_exact={c:.6f}")
+    assert e <= TOL_EMU
+    assert c >= COS_MIN
+    lse = to_np(plan.lse)
+    assert np.abs(lse - lse_emu).max() < 1e-4
+
+
+@pytest.mark.parametrize("sparse", [(1, 10), (1, 4), (0, 1), (1, 1)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_mask_matches_oracle(gpu_lib, sparse, causal):
+    p, t = make_case(B=1, Hq=8, Hkv=2, N=4096, d=128, dtype="bf16", causal=causal, seed=31,
+                     k_offset_std=3.0, outliers=4)
+    log(f"block_mask causal={causal} keep={sparse}")
+    plan, o = run_gpu(gpu_lib, p, t, sparse=sparse)
+    ref = oracle.smooth_quant(t["q"], t["k"], pools=True)
+    idx, cnt, ties = oracle.block_mask(ref["q_pool"], ref["k_pool"], p.Hq, p.Hkv, causal,
+                                       sparse[0], sparse[1], plan.max_keep)
+    gi, gc = to_np(plan.kv_idx), to_np(plan.kv_cnt)
+    ok = ~ties
+    assert np.array_equal(gc[ok], cnt[ok])
+    assert np.array_equal(gi[ok], idx[ok])
+    # near-tie rows may swap one block; everything else about them is fixed
+    assert np.array_equal(gc, cnt)
+
+
+def test_sparse_fwd_matches_emulation(gpu_lib):
+    p, t = make_case(B=1, Hq=8, Hkv=2, N=2048, d=128, dtype="bf16", causal=True, seed=32,
+                     k_offset_std=3.0, outliers=4, sparse=(1, 10))
+    log("sparse fwd N=2048")
+    plan, o = run_gpu(gpu_lib, p, t, sparse=(1, 10))
+    idx, cnt = to_np(plan.kv_idx).astype(np.int32), to_np(plan.kv_cnt).astype(np.int32)
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    O_emu, O_pre, _ = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
+                                               sq["k_scale"], t["v"], True, p.Hq, p.Hkv,
+                                               kv_idx=idx, kv_cnt=cnt)
+    O_ex, _ = oracle.exact_attention(t["q"], t["k"], t["v"], True, idx, cnt)
+    og = to_np(o)
+    e, c = out_err(og, O_pre, p.dtype), cos(og, O_ex)
+    log(f"  err_vs_emu={e:.3e} cos_exact_same_mask={c:.6f}")
+    assert e <= TOL_EMU and c >= COS_MIN
+
+
+def test_keep_all_mask_equals_dense_bit_exact(gpu_lib):
+    p, t = make_case(B=1, Hq=4, Hkv=2, N=1024, d=128, dtype="bf16", causal=True, seed=33,
+                     k_offset_std=3.0)
+    _, o_dense = run_gpu(gpu_lib, p, t)
+    _, o_sparse = run_gpu(gpu_lib, p, t, sparse=(1, 1))
+    assert torch.equal(o_dense, o_sparse)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_closed_forms_v_ones_and_causal_row0(gpu_lib, dtype):
+    p, t = make_case(B=1, Hq=4, Hkv=2, N=512, d=128, dtype=dtype, causal=True, seed=34,
+                     k_offset_std=3.0)
+    t1 = dict(t, v=torch.ones_like(t["v"]))
+    _, o = run_gpu(gpu_lib, p, t1)
+    assert torch.all(o == 1)
+    _, o = run_gpu(gpu_lib, p, t)
+    v = t["v"].to("cuda:0")
+    for hq in range(4):
+        assert torch.equal(o[0, hq, 0], v[0, hq // 2, 0])
+
+
+def test_deterministic_and_no_stray_writes(gpu_lib):
+    p, t = make_case(B=1, Hq=4, Hkv=2, N=1024, d=64, dtype="bf16", causal=True, seed=35)
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    qa = gpu_lib
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
+                   sparse=(1, 10), with_lse=True)
+    guard = 4096
+    buf = torch.full((q.numel() + 2 * guard,), 12345.0, dtype=q.dtype, device=dev)
+    o = buf[guard:guard + q.numel()].view_as(q)
+    plan.run(q, k, v, o)
+    first = o.clone()
+    idx1 = plan.kv_idx.clone()
+    plan.run(q, k, v, o)
+    torch.cuda.synchronize()
+    assert torch.equal(first, o)
+    assert torch.equal(idx1, plan.kv_idx)
+    assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[-guard:] == 12345.0)
+
+
+# ---- the five workloads at full size, compared on sampled heads/blocks ------------
+
+def _sampled_check(qa, c, n_blocks=3):
+    p, t = make_config(c)
+    log(f"config {c}: {p.name}")
+    sparse = p.sparse
+    plan, o = run_gpu(qa, p, t, sparse=sparse, pools=True)
+    b = p.B - 1
+    hk = p.Hkv - 1
+    hqs = [hk * p.group, hk * p.group + p.group - 1] if p.group > 1 else [hk]
+    sub, _ = head_slice(t, p, b, hqs)
+    ps = dataclasses.replace(p, B=1, Hq=len(hqs), Hkv=1)
+    ref = oracle.smooth_quant(sub["q"], sub["k"], pools=sparse is not None)
+    # bit-exact pre-processing on the slice
+    assert np.array_equal(to_np(plan.k_mean)[b, hk], ref["k_mean"][0, 0])
+    assert np.array_equal(to_np(plan.k_scale)[b, hk], ref["k_scale"][0, 0])
+    assert np.array_equal(to_np(plan.k_i8[b, hk]), ref["k_i8"][0, 0])
+    for n, hq in enumerate(hqs):
+        assert np.array_equal(to_np(plan.q_scale)[b, hq], ref["q_scale"][0, n])
+        assert np.array_equal(to_np(plan.q_i8[b, hq]), ref["q_i8"][0, n])
+    nqb = p.N // 128
+    blocks = sorted({0, nqb // 2, nqb - 1})[:n_blocks]
+    sel = [(0, n, i) for n in range(len(hqs)) for i in blocks]
+    kv_idx = kv_cnt = None
+    if sparse is not None:
+        assert np.array_equal(to_np(plan.q_pool)[b, hqs], ref["q_pool"][0])
+        assert np.array_equal(to_np(plan.k_pool)[b, hk], ref["k_pool"][0, 0])
+        idx, cnt, ties = oracle.block_mask(ref["q_pool"], ref["k_pool"], len(hqs), 1, p.causal,
+                                           sparse[0], sparse[1], plan.max_keep)
+        gi = to_np(plan.kv_idx)[b, hqs]
+        gc = to_np(plan.kv_cnt)[b, hqs]
+        ok = ~ties[0]
+        assert np.array_equal(gc, cnt[0])
+        assert np.array_equal(gi[ok], idx[0][ok])
+        kv_idx, kv_cnt = gi[None].astype(np.int32), gc[None].astype(np.int32)
+    O_emu, O_pre, _ = oracle.emulate_attention(ref["q_i8"], ref["q_scale"], ref["k_i8"],
+                                               ref["k_scale"], sub["v"], p.causal, ps.Hq, 1,
+                                               kv_idx=kv_idx, kv_cnt=kv_cnt, blocks=sel)
+    O_ex, _ = oracle.exact_attention(sub["q"], sub["k"], sub["v"], p.causal, kv_idx, kv_cnt,
+                                     blocks=sel)
+    og = to_np(o[b, hqs])[None]
+    rows = np.concatenate([np.arange(i * 128, i * 128 + 128) for i in blocks])
+    g = og[:, :, rows]
+    e = out_err(g, O_pre[:, :, rows], p.dtype)
+    cc = cos(g, O_ex[:, :, rows])
+    log(f"  sampled {len(sel)} blocks: err_vs_emu={e:.3e} cos_exact={cc:.6f}")
+    assert e <= TOL_EMU
+    assert cc >= COS_MIN
+
+
+@pytest.mark.parametrize("c", [2, 3, 5])
+def test_workload_full_size_sampled(gpu_lib, c):
+    _sampled_check(gpu_lib, c)
+
+
+def test_workload_c4_full_size_sampled(gpu_lib):
+    _sampled_check(gpu_lib, 4, n_blocks=2)
