@@ -1,0 +1,228 @@
+"""Benchmark of the quantized attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of the workload's seeded
+synthetic input (already resident in HBM): qattn_smooth_quant, then
+qattn_block_mask for the block-sparse workload, then qattn_fwd. The default
+workload is the Llama-3.1-8B-shaped causal prefill (B=1, Hq=32, Hkv=8,
+N=8192, d=128, bf16).
+
+Prints one JSON line. ``value`` is the attention metric 4*N^2*d*H*B / step time
+in TOPS (dense-equivalent operation count, the whole step in the denominator).
+``roofline`` describes the dominant kernel (attn_fwd): its algorithmic
+operations per launch (causal: 4*d*H*B*N(N+1)/2; sparse: 4*d*64*rows over the
+kept tiles) over its average launch time, measured with HIP events on the
+launch stream, against the INT8 dense matrix peak. ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 matrix peak (TOPS)
+PEAK_BF16_TFLOPS = 2500.0     # dense FP16/BF16 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def dense_algorithmic_ops(p) -> float:
+    """Operations the method performs on a dense problem: 2*d per (query,
+    visible key) for Q K^T and 2*d for P V (causal: key <= query)."""
+    pairs = p.N * (p.N + 1) / 2 if p.causal else float(p.N) * p.N
+    return 4.0 * p.d * pairs * p.Hq * p.B
+
+
+def sparse_pairs(kv_idx: np.ndarray, kv_cnt: np.ndarray, causal: bool) -> float:
+    """Visible (query, key) pairs under a keep list [B,Hq,nqb,mk]."""
+    total = 0
+    B, H, nqb, _ = kv_idx.shape
+    rows = np.arange(128)
+    for i in range(nqb):
+        q = 128 * i + rows
+        lst = kv_idx[:, :, i, :]
+        cnt = kv_cnt[:, :, i]
+        for j in np.unique(lst[lst >= 0]):
+            keys = 64 * j + np.arange(64)
+            vis = int((keys[None, :] <= q[:, None]).sum()) if causal else 128 * 64
+            # number of (b, h) rows keeping block j
+            n = int(((lst == j) & (np.arange(lst.shape[-1])[None, None, :] < cnt[..., None])).sum())
+            total += vis * n
+    return float(total)
+
+
+def run_cpu_baseline(p, t, target_s: float):
+    """The oracle, as it stands, on a bounded sample: every query block of as many
+    query heads as fit in about target_s seconds (after the head's group is
+    smoothed and quantized, and masked when sparse)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+        threads = max([n for _, n in blas if n] or [1])
+    except Exception:  # pragma: no cover
+        blas, threads = [], 1
+    b = 0
+    done_ops = 0.0
+    heads_done = 0
+    t0 = time.perf_counter()
+    nqb = p.N // 128
+    for hk in range(p.Hkv):
+        hqs = list(range(hk * p.group, (hk + 1) * p.group))
+        q = t["q"][b:b + 1, hqs].contiguous()
+        k = t["k"][b:b + 1, hk:hk + 1].contiguous()
+        v = t["v"][b:b + 1, hk:hk + 1].contiguous()
+        sparse = p.sparse is not None
+        sq = oracle.smooth_quant(q, k, pools=sparse)
+        idx = cnt = None
+        if sparse:
+            num, den = p.sparse
+            idx, cnt, _ = oracle.block_mask(sq["q_pool"], sq["k_pool"], len(hqs), 1, p.causal,
+                                            num, den)
+        for n in range(len(hqs)):
+            blocks = [(0, n, i) for i in range(nqb)]
+            oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], v,
+                                     p.causal, len(hqs), 1, kv_idx=idx, kv_cnt=cnt,
+                                     blocks=blocks)
+            heads_done += 1
+            if sparse:
+                done_ops += 4.0 * p.d * sparse_pairs(idx[:, n:n + 1], cnt[:, n:n + 1], p.causal)
+            else:
+                pairs = p.N * (p.N + 1) / 2 if p.causal else float(p.N) ** 2
+                done_ops += 4.0 * p.d * pairs
+            if time.perf_counter() - t0 >= target_s:
+                break
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": done_ops / el / 1e12,
+        "unit": "TOPS (algorithmic)",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"oracle smooth_quant + {'block_mask + ' if p.sparse else ''}emulate_attention "
+                  f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
+                  f"({el:.1f} s); numpy BLAS {blas}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_attention_amd as qa
+    from synthetic import make_config
+
+    qa.load()
+    p, t = make_config(args.config)
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
+                   sparse=p.sparse)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan.run(q, k, v, o)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps; the attention kernel's own launches are
+    # bracketed by events on the same stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    sq_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        sq_ev[s][0].record(stream)
+        plan.smooth_quant(q, k)
+        if p.sparse is not None:
+            plan.block_mask()
+        sq_ev[s][1].record(stream)
+        ev[s][0].record(stream)
+        plan.fwd(v, o)
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    fwd_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pre_ms = np.array([a.elapsed_time(b) for a, b in sq_ev])
+    fwd_avg = float(fwd_ms.mean())
+
+    literal = 4.0 * p.N * p.N * p.d * p.Hq * p.B
+    if p.sparse is not None:
+        pairs = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
+        alg = 4.0 * p.d * pairs
+    else:
+        alg = dense_algorithmic_ops(p)
+    achieved = alg / (fwd_avg * 1e-3) / 1e12
+    # Q: read 2 B + write 1 B per element; K: two reads of 2 B + write 1 B
+    pre_bytes = (p.B * p.Hq * p.N * p.d * 3 + p.B * p.Hkv * p.N * p.d * 5)
+    res = {
+        "metric": "attention TOPS (4*N^2*d*H/s) at N=8K and 64K; % of INT8 MFMA peak",
+        "value": literal / (ms_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+bf16" if p.dtype == "bf16" else "i8+f16",
+        "data": "synthetic (seeded Gaussian Q/K/V with per-channel K offsets and outlier channels)",
+        "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
+                   "causal": p.causal, "sparse": p.sparse, "input_dtype": p.dtype},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_INT8_TOPS,
+            "traffic": None,
+            "kernel": "attn_fwd",
+            "algorithmic_ops_per_launch": alg,
+            "avg_launch_ms": fwd_avg,
+        },
+        "fwd_ms": fwd_avg,
+        "fwd_tops_literal": literal / (fwd_avg * 1e-3) / 1e12,
+        "fwd_tops_algorithmic": achieved,
+        "preprocess_ms": float(pre_ms.mean()),
+        "preprocess_gbs_algorithmic": pre_bytes / (float(pre_ms.mean()) * 1e-3) / 1e9
+        if p.sparse is None else None,
+        "blended_mfma_peak_tops": 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -131,7 +131,8 @@ qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const flo
   for (const void* x : ptrs)
     if (x && misaligned(x)) return QATTN_ERR_ALIGN;
   if ((kv_idx == nullptr) != (kv_cnt == nullptr)) return QATTN_ERR_ARG;
-  if (kv_idx != nullptr && max_keep < 1) return QATTN_ERR_ARG;
+  if (kv_idx != nullptr && (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()))
+    return QATTN_ERR_ARG;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
                                          max_keep, o, lse, static_cast<hipStream_t>(stream)));
 }

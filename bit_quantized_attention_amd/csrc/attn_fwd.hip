@@ -1,21 +1,39 @@
 // Quantized attention forward on gfx950 matrix cores.
 //
-// Work decomposition: one workgroup of two waves per (b, hq, 128-row query
-// block); each wave owns 64 query rows (two 32-column MFMA blocks). The grid is
-// ordered so that workgroups of one kv head land on one XCD (blockIdx % 8
-// selects the XCD) and, for causal masking, the longest rows start first.
+// Work decomposition. A wave owns 64 query rows of one query head (two
+// 32-column MFMA blocks). Dense: a workgroup of 4 waves takes g4 = gcd(group,4)
+// query heads of one kv head times 4/g4 row chunks, so the 4 waves share every
+// K/V tile they stage (for GQA group 4: four heads, the same 64 rows). Sparse:
+// a workgroup of 2 waves takes one 128-row query block of one head (its kept
+// list is the workgroup's tile list). Consecutive workgroups map to distinct
+// kv heads, so blockIdx % 8 (the XCD) keeps each kv head on one XCD's L2;
+// under causal masking the longest rows are dispatched first.
 //
-// Data flow per 64-key tile (all in registers except the K/V staging):
-//   S^T[key][q] = K_tile . Q^T           v_mfma_i32_32x32x32_i8, 2x2 blocks
-//   online softmax on S^T columns        each lane owns one query column per
-//                                        block (lanes l and l+32 hold the two
-//                                        halves of its 32 keys)
-//   O^T[d][q] += V^T . P^T               v_mfma_f32_32x32x16_{bf16,f16}
-// Computing the transposed products makes the INT8 accumulator layout (lane =
-// column, registers = rows) exactly the B-operand layout of the 16-bit MFMA, so
-// P never leaves registers. K is staged row-major in LDS, V transposed (V^T),
-// both with padded rows so the 16- and 8-byte fragment reads are free of bank
-// conflicts.
+// Per 64-key tile (registers except the K/V staging):
+//   S^T[key][q] = K_tile . Q^T       v_mfma_i32_32x32x32_i8, 2x2 blocks, 4/2 k-steps
+//   online base-2 softmax on S^T     lane = query column; lanes l, l+32 hold the
+//                                    two halves of its 32 keys per block
+//   O^T[d][q] += V^T . P^T           v_mfma_f32_32x32x16_{bf16,f16}
+// The transposed products make the INT8 accumulator layout (lane = column,
+// registers = rows) the B-operand layout of the 16-bit MFMA: P never leaves
+// registers. K and V are staged row-major in LDS by direct global->LDS loads
+// (global_load_lds_dwordx4: one wave instruction fills 1 KB); each row's
+// 16-byte slots are XOR-swizzled by the row index so that the 16-byte K
+// fragment reads and the 8-byte transposing V reads are free of bank
+// conflicts. The V^T operand comes from ds_read_b64_tr_b16, which hands each
+// lane 4 consecutive keys of one channel.
+//
+// Pipeline: K is staged two tiles ahead and V one tile ahead (double buffers,
+// asynchronous loads issued at the top of an iteration and waited for at its
+// end, one barrier per tile); S of tile t+1 is computed before P V of tile t
+// so the matrix cores have independent work while the softmax of tile t runs.
+//
+// Online softmax reference: a row's exponent reference m moves only when the
+// tile's running max exceeds it by more than kTau (log2 units); otherwise P is
+// taken against the stale reference (P <= 2^kTau) and the accumulator is not
+// rescaled. The move test is wave-uniform, so the rescale is skipped for the
+// whole wave in the common case.
+#include "../../include/qattn.h"
 #include "device_util.h"
 #include "qattn_internal.h"
 
@@ -25,8 +43,20 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+constexpr int kKT = 64;             // keys per tile
+constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
+constexpr int kMaxSparseTiles = 2048;
+
+#ifndef QATTN_PINGPONG
+#define QATTN_PINGPONG 0
+#endif
 
 template <bool BF16>
 struct Mma16;
@@ -34,20 +64,35 @@ struct Mma16;
 template <>
 struct Mma16<true> {
   typedef v8bf op_t;
+  typedef v2bf pair_t;
   typedef __bf16 el_t;
   static __device__ __forceinline__ v16f mma(op_t a, op_t b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // sum of the two 16-bit values of a pair, accumulated in fp32
+  static __device__ __forceinline__ float sum2(pair_t p, float acc) {
+    const pair_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
   }
 };
 
 template <>
 struct Mma16<false> {
   typedef v8h op_t;
+  typedef v2h pair_t;
   typedef _Float16 el_t;
   static __device__ __forceinline__ v16f mma(op_t a, op_t b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ float sum2(pair_t p, float acc) {
+    const pair_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(p, one, acc, false);
+  }
 };
+
+__device__ __forceinline__ v4s lds_read_tr16(const int8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+}
 
 struct FwdArgs {
   const int8_t* q_i8;
@@ -59,133 +104,199 @@ struct FwdArgs {
   float* lse;
   const int32_t* kv_idx;
   const int32_t* kv_cnt;
-  int B, Hq, Hkv, N, group, nqb, nkb, max_keep;
+  int B, Hq, Hkv, N, group, g4, nqb, nkb, max_keep;
   float c;  // fl32(log2(e) / sqrt(d))
 };
 
-constexpr int kThreads = 128;  // two waves
-constexpr int kKT = 64;        // keys per tile
+template <int D>
+struct Geo {
+  static constexpr int KROW = D;           // K row in LDS (bytes, unpadded)
+  static constexpr int VROW = 2 * D;       // V row in LDS (bytes, unpadded)
+  static constexpr int KBUF = kKT * KROW;
+  static constexpr int VBUF = kKT * VROW;
+  static constexpr int KS = D / 32;        // 32-deep k-steps of the INT8 product
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int KSLOTS = D / 16;    // 16-byte slots per K row
+  static constexpr int VSLOTS = D / 8;     // 16-byte slots per V row
+  // swizzle of a K row: slot s of row r holds chunk s ^ kswz(r); spreads the 8
+  // rows read together (one per lane of an 8-lane phase) over all banks
+  static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); }
+  // swizzle of a V row: the 4 rows a 16-lane transposing read touches land on
+  // disjoint 32-byte bank groups
+  static __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+};
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__device__ __forceinline__ void lds_dma16(const void* g, int8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+}
+
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
   using op_t = typename MM::op_t;
+  using pair_t = typename MM::pair_t;
   using el_t = typename MM::el_t;
-  constexpr int KSTR = D + 16;   // bytes per K row in LDS
-  constexpr int VSTR = kKT + 4;  // elements per V^T row in LDS
-  constexpr int KS = D / 32;     // 32-deep k-steps of the INT8 product
-  constexpr int DB = D / 32;     // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) int8_t k_lds[kKT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTR];
+  using G = Geo<D>;
+  constexpr int KPW = G::KBUF / 1024 / NW;  // 1 KB direct loads per wave per K tile
+  constexpr int VPW = G::VBUF / 1024 / NW;  // same for V
+  static_assert(KPW >= 1 && VPW >= 1, "tile too small for the workgroup");
+  __shared__ __attribute__((aligned(16))) int8_t k_lds[2][G::KBUF];
+  __shared__ __attribute__((aligned(16))) int8_t v_lds[2][G::VBUF];
+  __shared__ int tile_list[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int n_list;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-
-  // ---- work item -------------------------------------------------------------
-  const int nheads = a.B * a.Hq;
-  const int slot = blockIdx.x % nheads;
-  const int rank = blockIdx.x / nheads;
   const int nkvu = a.B * a.Hkv;
-  const int kvu = slot % nkvu;         // b * Hkv + hk: consecutive blocks, distinct XCDs
-  const int g = slot / nkvu;
-  const int b = kvu / a.Hkv;
-  const int hk = kvu % a.Hkv;
-  const int hq = hk * a.group + g;
-  const int i = CAUSAL ? (a.nqb - 1 - rank) : rank;
-  const size_t bhq = (size_t)b * a.Hq + hq;
-  const int row0 = i * kQBlock + wave * 64;  // first query row of this wave
 
-  // ---- Q fragments (B operand of S^T = K Q^T) ---------------------------------
-  v4i qf[2][KS];
-  {
+  // ---- work item ---------------------------------------------------------------
+  int kvu, hq, row0, wg_last_row, qblk;
+  if constexpr (SPARSE) {
+    const int nheads = a.B * a.Hq;
+    const int slot = blockIdx.x % nheads;
+    const int rank = blockIdx.x / nheads;
+    kvu = slot % nkvu;
+    const int g = slot / nkvu;
+    hq = (kvu % a.Hkv) * a.group + g;
+    qblk = CAUSAL ? (a.nqb - 1 - rank) : rank;
+    row0 = qblk * kQBlock + 64 * wave;
+    wg_last_row = qblk * kQBlock + kQBlock - 1;
+  } else {
+    const int g4 = a.g4;
+    const int rows_wg = 64 * (NW / g4);
+    const int nrc = (a.N + rows_wg - 1) / rows_wg;
+    const int nsub = a.group / g4;
+    const int nslot = nkvu * nsub;
+    const int slot = blockIdx.x % nslot;
+    const int rank = blockIdx.x / nslot;
+    kvu = slot % nkvu;
+    const int hs = slot / nkvu;
+    const int rc = CAUSAL ? (nrc - 1 - rank) : rank;
+    hq = (kvu % a.Hkv) * a.group + hs * g4 + wave % g4;
+    row0 = rc * rows_wg + 64 * (wave / g4);
+    wg_last_row = min(a.N, rc * rows_wg + rows_wg) - 1;
+    qblk = row0 / kQBlock;
+  }
+  const int b = kvu / a.Hkv;
+  const size_t bhq = (size_t)b * a.Hq + hq;
+  const bool wave_live = row0 < a.N;  // wave-uniform
+  const size_t kv_row0 = (size_t)kvu * a.N;
+
+  // ---- tile list -----------------------------------------------------------------
+  int ntiles;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
+      const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      int n = 0;
+      for (int e0 = 0; e0 < cnt; e0 += 64) {
+        const int e = e0 + lane;
+        const int t = e < cnt ? src[e] : -1;
+        const bool ok = t >= 0 && t < a.nkb && (!CAUSAL || t * kKT <= wg_last_row);
+        const uint64_t bal = __ballot(ok);
+        if (ok) tile_list[n + __popcll(bal & lt)] = t;
+        n += __popcll(bal);
+      }
+      if (lane == 0) n_list = n;
+    }
+    __syncthreads();
+    ntiles = n_list;
+  } else {
+    ntiles = CAUSAL ? wg_last_row / kKT + 1 : a.nkb;
+  }
+  auto tile_of = [&](int it) -> int {
+    if constexpr (SPARSE) return tile_list[it];
+    else return it;
+  };
+  // causal: the last tile this wave sees is its diagonal tile row0 / 64
+  auto wave_needs = [&](int t) -> bool { return wave_live && (!CAUSAL || t * kKT <= row0); };
+
+  // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------------
+  v4i qf[2][G::KS];
+  if (wave_live) {
     const int8_t* qg = a.q_i8 + (bhq * a.N + row0) * D;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < G::KS; ++ks)
         qf[qb][ks] = *reinterpret_cast<const v4i*>(qg + (size_t)(32 * qb + l32) * D + 32 * ks + 16 * h);
   }
-  const float alpha_q = a.q_scale[bhq * a.nqb + i] * a.c;
+  const float alpha_q = wave_live ? a.q_scale[bhq * a.nqb + qblk] * a.c : 0.0f;
+  const float* kscale = a.k_scale + (size_t)kvu * a.nkb;
 
-  v16f acc[DB][2];
+  v16f acc[G::DB][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < G::DB; ++db)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.0f;
-  float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.0f, 0.0f};  // this lane's half of the row sum
+  float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
+  float l_run[2] = {0.0f, 0.0f};  // this lane's half of each row sum
 
-  int ntiles;
-  const int32_t* klist = nullptr;
-  if constexpr (SPARSE) {
-    ntiles = min(a.kv_cnt[bhq * a.nqb + i], a.max_keep);
-    klist = a.kv_idx + (bhq * a.nqb + i) * a.max_keep;
-  } else {
-    ntiles = CAUSAL ? 2 * i + 2 : a.nkb;
-  }
-  const int last_tile_wave = row0 / kKT;  // causal: last tile this wave sees (its diagonal)
-  const size_t kv_row0 = (size_t)kvu * a.N;
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int t = SPARSE ? klist[it] : it;
-    if (SPARSE) {
-      // ignore entries outside the block range or past the causal range
-      if (t < 0 || t >= a.nkb) continue;
-      if (CAUSAL && t * kKT > i * kQBlock + kQBlock - 1) continue;
-    }
-    __syncthreads();  // previous tile's LDS readers are done
-    {
-      const int8_t* kg = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D;
-      constexpr int CPR = D / 16;
-      for (int c = threadIdx.x; c < kKT * CPR; c += kThreads) {
-        const int r = c / CPR, col = c % CPR;
-        *reinterpret_cast<int4*>(&k_lds[r * KSTR + col * 16]) =
-            *reinterpret_cast<const int4*>(kg + (size_t)r * D + col * 16);
-      }
-      const uint16_t* vg = a.v + (kv_row0 + (size_t)t * kKT) * D;
-      constexpr int EPR = D / 8;
-      for (int c = threadIdx.x; c < kKT * EPR; c += kThreads) {
-        const int key = c / EPR, d0 = (c % EPR) * 8;
-        const uint4 w = *reinterpret_cast<const uint4*>(vg + (size_t)key * D + d0);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  // ---- staging: direct global -> LDS, 1 KB per wave instruction -------------------
+  // K piece p holds rows (1024/KROW)*p ..; lane l writes slot l % KSLOTS of row
+  // l / KSLOTS, i.e. the global chunk (slot ^ kswz(row)).
+  const int k_lane_src = [&] {
+    const int r = lane / G::KSLOTS, sl = lane % G::KSLOTS;
+    return r * G::KROW + ((sl ^ G::kswz(r)) * 16);
+  }();
+  const int v_lane_src = [&] {
+    const int r = lane / G::VSLOTS, sl = lane % G::VSLOTS;
+    return r * G::VROW + ((sl ^ G::vswz(r)) * 16);
+  }();
+  auto load_k = [&](int t, int buf) {
+    const int8_t* src = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D + k_lane_src;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt_lds[(d0 + 2 * e) * VSTR + key] = (uint16_t)(ws[e] & 0xffffu);
-          vt_lds[(d0 + 2 * e + 1) * VSTR + key] = (uint16_t)(ws[e] >> 16);
+    for (int j = 0; j < KPW; ++j) {
+      const int piece = wave + NW * j;
+      lds_dma16(src + piece * 1024, &k_lds[buf][piece * 1024]);
+    }
+  };
+  auto load_v = [&](int t, int buf) {
+    const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)t * kKT) * D) + v_lane_src;
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+      const int piece = wave + NW * j;
+      lds_dma16(src + piece * 1024, &v_lds[buf][piece * 1024]);
+    }
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // ---- compute helpers -----------------------------------------------------------
+  // K fragment (key row kb*32 + l32, chunk 2*ks + h), swizzled; kb*32 keeps kswz
+  int k_frag_off[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
+  auto qk = [&](int buf, v16i (&s)[2][2]) {
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const v4i kf = *reinterpret_cast<const v4i*>(&k_lds[buf][kb * 32 * G::KROW + k_frag_off[ks]]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (ks == 0) {
+            const v16i zero = {};
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], zero, 0, 0, 0);
+          } else {
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();
-    if (CAUSAL && t > last_tile_wave) continue;  // wave-uniform: all keys masked
-    const bool diag = CAUSAL && t == last_tile_wave;
+  };
 
-    // ---- S^T = K Q^T (INT8) ---------------------------------------------------
-    v16i sacc[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][qb][r] = 0;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const v4i kf = *reinterpret_cast<const v4i*>(&k_lds[(kb * 32 + l32) * KSTR + 32 * ks + 16 * h]);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], sacc[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax, one query column per lane and block ------------------
-    const float alpha = alpha_q * a.k_scale[(size_t)kvu * a.nkb + t];
-    op_t pf[2][2][2];  // [kb][qb][half of the 32 keys]
+  // softmax of one tile, one 32-query block at a time: S (exact int32) -> P
+  // packed in the B-operand layout of the P V product
+  auto softmax = [&](const v16i (&s)[2][2], int t, op_t (&pf)[2][2][2]) {
+    const float alpha = alpha_q * kscale[t];
+    const bool diag = CAUSAL && t * kKT == row0;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float f[2][16];
@@ -194,59 +305,129 @@ void attn_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = (float)sacc[kb][qb][r];
+          float x = (float)s[kb][qb][r];
           if (diag) {
             const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            const int q = 32 * qb + l32;
-            if (key > q) x = -__builtin_inff();
+            if (key > 32 * qb + l32) x = -__builtin_inff();
           }
           f[kb][r] = x;
           mx = __builtin_fmaxf(mx, x);
         }
       mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = __builtin_fmaxf(m_run[qb], mx * alpha);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-      const float corr = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
-      m_run[qb] = m_new;
-      float psum = 0.0f;
+      const float mc = __builtin_fmaxf(m_ref[qb], mx * alpha);
+      const bool move = mc > m_ref[qb] + kTau;
+      if (__ballot(move) != 0) {
+        float corr = 1.0f;
+        if (move) {
+          corr = (m_ref[qb] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_ref[qb] - mc);
+          m_ref[qb] = mc;
+        }
+        l_run[qb] *= corr;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr;
+      }
+      const float m_use = (m_ref[qb] == -__builtin_inff()) ? 0.0f : m_ref[qb];
+      float lsum = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int half = 0; half < 2; ++half) {
+          op_t pk;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(f[kb][8 * half + e], alpha, -m_use));
-            const el_t pe = (el_t)p;
-            psum += (float)pe;
-            pf[kb][qb][half][e] = pe;
+          for (int e = 0; e < 8; ++e)
+            pk[e] = (el_t)__builtin_amdgcn_exp2f(__builtin_fmaf(f[kb][8 * half + e], alpha, -m_use));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const pair_t pr = {pk[e], pk[e + 1]};
+            lsum = MM::sum2(pr, lsum);
           }
-      l_run[qb] = l_run[qb] * corr + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr;
+          pf[kb][qb][half] = pk;
+        }
+      l_run[qb] += lsum;
     }
+  };
 
-    // ---- O^T += V^T P^T (16-bit operands, fp32 accumulate) -------------------
+  // transposing V reads: 16-lane group g = lane/16 reads key rows
+  // k0 + 4*(g/2) + (lane%16)/4 and the 32 bytes of channels
+  // 32*db + 16*(g%2) + [0, 16); lane j of the group takes 8 of them. The row's
+  // low two bits (the swizzle input) depend on the lane only.
+  const int grp = lane >> 4;
+  const int vr_lane = 4 * (grp >> 1) + ((lane >> 2) & 3);
+  int v_frag_off[G::DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < G::DB; ++db) {
+    const int slot = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
+    v_frag_off[db] = vr_lane * G::VROW + ((slot ^ G::vswz(vr_lane)) * 16) + 8 * (lane & 1);
+  }
+  auto pv = [&](int buf, const op_t (&pf)[2][2][2]) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const uint16_t* vr = &vt_lds[(db * 32 + l32) * VSTR + kb * 32 + 16 * half + 4 * h];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          const v4i raw = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-          const op_t vf = __builtin_bit_cast(op_t, raw);
+          const int8_t* p = &v_lds[buf][(kb * 32 + 16 * half) * G::VROW + v_frag_off[db]];
+          const v4s lo = lds_read_tr16(p);
+          const v4s hi = lds_read_tr16(p + 8 * G::VROW);
+          const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const op_t vf = __builtin_bit_cast(op_t, both);
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb) acc[db][qb] = MM::mma(vf, pf[kb][qb][half], acc[db][qb]);
         }
-      }
-    }
-  }
+  };
 
-  // ---- epilogue: O = acc / l, lse -------------------------------------------------
+  // ---- pipeline ---------------------------------------------------------------------
+  if (ntiles > 0) {
+    load_k(tile_of(0), 0);
+    load_v(tile_of(0), 0);
+    if (ntiles > 1) load_k(tile_of(1), 1);
+  }
+  wait_loads();
+  __syncthreads();
+
+  v16i s_a[2][2], s_b[2][2];
+  if (ntiles > 0 && wave_needs(tile_of(0))) qk(0, s_a);
+
+  auto step = [&](int it, v16i (&s_cur)[2][2], v16i (&s_nxt)[2][2]) {
+    const int t = tile_of(it);
+    const bool pre_k = it + 2 < ntiles;
+    const bool pre_v = it + 1 < ntiles;
+    // K(it) and V(it-1) were consumed before the last barrier: their buffers
+    // take K(it+2) and V(it+1)
+    if (pre_k) load_k(tile_of(it + 2), it & 1);
+    if (pre_v) load_v(tile_of(it + 1), (it + 1) & 1);
+    const bool cur = wave_needs(t);
+    const bool nxt = pre_v && wave_needs(tile_of(it + 1));
+    op_t pf[2][2][2];
+#if QATTN_PINGPONG
+    if (cur) softmax(s_cur, t, pf);
+    if (nxt) qk((it + 1) & 1, s_nxt);
+    if (cur) pv(it & 1, pf);
+#else
+    if (cur) {
+      softmax(s_cur, t, pf);
+      pv(it & 1, pf);
+    }
+    if (nxt) qk((it + 1) & 1, s_cur);
+    (void)s_nxt;
+#endif
+    wait_loads();
+    __syncthreads();
+  };
+
+  int it = 0;
+#if QATTN_PINGPONG
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, s_a, s_b);
+    step(it + 1, s_b, s_a);
+  }
+#endif
+  for (; it < ntiles; ++it) step(it, s_a, s_b);
+
+  // ---- epilogue: O = acc / l, lse --------------------------------------------------
+  if (!wave_live) return;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
@@ -254,45 +435,50 @@ void attn_fwd_kernel(FwdArgs a) {
     const int q = row0 + 32 * qb + l32;
     uint16_t* og = a.o + (bhq * a.N + q) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
+      for (int g = 0; g < 4; ++g) {
         uint16_t e16[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const el_t y = (el_t)(acc[db][qb][4 * grp + e] * inv);
+          const el_t y = (el_t)(acc[db][qb][4 * g + e] * inv);
           e16[e] = __builtin_bit_cast(uint16_t, y);
         }
         uint2 w;
         w.x = (uint32_t)e16[0] | ((uint32_t)e16[1] << 16);
         w.y = (uint32_t)e16[2] | ((uint32_t)e16[3] << 16);
-        *reinterpret_cast<uint2*>(og + db * 32 + 8 * grp + 4 * h) = w;
+        *reinterpret_cast<uint2*>(og + db * 32 + 8 * g + 4 * h) = w;
       }
     if (a.lse != nullptr && h == 0) {
       a.lse[bhq * a.N + q] =
-          lt > 0.0f ? 0.69314718055994531f * (m_run[qb] + __builtin_log2f(lt)) : -__builtin_inff();
+          lt > 0.0f ? 0.69314718055994531f * (m_ref[qb] + __builtin_log2f(lt)) : -__builtin_inff();
     }
   }
 }
 
-template <int D, bool BF16>
-hipError_t launch_d(const FwdArgs& a, bool causal, bool sparse, hipStream_t stream) {
-  const dim3 grid(a.B * a.Hq * a.nqb), block(kThreads);
-  if (causal) {
-    if (sparse)
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, true, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, true, false>), grid, block, 0, stream, a);
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
+  if (sparse) {
+    const dim3 grid(a.B * a.Hq * a.nqb);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 2>), grid, dim3(128), 0, stream, a);
   } else {
-    if (sparse)
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, false, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, false, false>), grid, block, 0, stream, a);
+    const int rows_wg = 64 * (4 / a.g4);
+    const int nrc = (a.N + rows_wg - 1) / rows_wg;
+    const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, 4>), grid, dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
 
+template <int D, bool BF16>
+hipError_t launch_d(const FwdArgs& a, bool causal, bool sparse, hipStream_t stream) {
+  return causal ? launch_dc<D, BF16, true>(a, sparse, stream)
+                : launch_dc<D, BF16, false>(a, sparse, stream);
+}
+
 }  // namespace
+
+int fwd_max_sparse_tiles() { return kMaxSparseTiles; }
 
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
@@ -313,6 +499,7 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
   a.Hkv = s.Hkv;
   a.N = s.N;
   a.group = s.Hq / s.Hkv;
+  a.g4 = (a.group % 4 == 0) ? 4 : (a.group % 2 == 0) ? 2 : 1;
   a.nqb = s.nqb();
   a.nkb = s.nkb();
   a.max_keep = max_keep;

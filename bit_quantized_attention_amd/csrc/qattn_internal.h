@@ -39,6 +39,9 @@ hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k
                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
                              int32_t* kv_cnt, void* workspace, hipStream_t stream);
 
+// Longest kept list qattn_fwd accepts (entries per query block).
+int fwd_max_sparse_tiles();
+
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,

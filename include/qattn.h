@@ -66,6 +66,9 @@ typedef struct {
 #define QATTN_Q_BLOCK 128
 #define QATTN_K_BLOCK 64
 #define QATTN_KV_TILE 64
+/* Online-softmax reference threshold (log2 units): a row's exponent reference
+ * moves to the running max only when the max exceeds it by more than this. */
+#define QATTN_SOFTMAX_REF_THRESHOLD 8
 
 /* Message for a status code (static storage, never NULL). */
 const char* qattn_status_str(qattn_status_t status);
@@ -166,7 +169,8 @@ qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool,
  *   S = q_codes k_codes^T (exact int32);
  *   alpha = fl32(fl32(q_scale * fl32(log2(e)/sqrt(d))) * k_scale);
  *   s = S * alpha, -inf where the key is masked;
- *   m' = max(m, rowmax s); P = exp2(s - m') rounded to V's dtype;
+ *   c = max(m, rowmax s); m' = c if c > m + QATTN_SOFTMAX_REF_THRESHOLD
+ *   (or m = -inf), else m' = m; P = exp2(s - m') rounded to V's dtype;
  *   l = l * exp2(m - m') + rowsum P; acc = acc * exp2(m - m') + P V (fp32);
  *   O = acc / l rounded to V's dtype; lse = ln2 * (m + log2 l), the natural
  *   log-sum-exp of the smoothed, dequantized logits (S * alpha / log2(e)).
@@ -178,7 +182,8 @@ qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool,
  * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL. A query row with
  *      no visible key gets O = 0 and lse = -inf.
  * Errors: NULL; SHAPE/UNSUPPORTED; ALIGN; ARG when exactly one of
- *      kv_idx/kv_cnt is NULL or max_keep < 1 with a mask; DEVICE.
+ *      kv_idx/kv_cnt is NULL, or with a mask when max_keep < 1 or
+ *      max_keep > 2048; DEVICE.
  */
 qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const float* q_scale,
                          const int8_t* k_i8, const float* k_scale, const void* v,

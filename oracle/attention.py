@@ -19,9 +19,15 @@ where the pages are silent:
   c = fl32(log2(e) / sqrt(d)), alpha_q = fl32(q_scale * c),
   alpha = fl32(alpha_q * k_scale[key block]), s = fl32(S * alpha);
   masked scores are -inf;
-* m_new = max(m_old, rowmax(s)); P = fl32(exp2(fl32(s - m_new)));
-  P_hat = P rounded to nearest-even in V's dtype (the 16-bit operand of the
-  P V product); corr = fl32(exp2(fl32(m_old - m_new)));
+* the exponent reference m of each row: m_cand = max(m, rowmax(s)); the
+  reference moves to m_cand only when m_cand > fl32(m + tau) (always on the
+  first visible key, m = -inf); otherwise it stays, so P may exceed 1 by up to
+  2^tau. tau = 0 is the textbook per-tile update; the kernel uses tau = 8
+  (its rescale of the accumulator is then almost never needed). In exact
+  arithmetic the result does not depend on the reference;
+* P = fl32(exp2(fl32(s - m_new))); P_hat = P rounded to nearest-even in V's
+  dtype (the 16-bit operand of the P V product);
+  corr = fl32(exp2(fl32(m_old - m_new))) (1 when the reference did not move);
   l = l * corr + sum(P_hat); acc = acc * corr + P_hat V, accumulated in fp64
   (the kernel accumulates in fp32: the 16-bit products are exact in either);
 * O = round_dtype(fl32(acc / l)); lse = ln(2) * (m + log2(l)), the natural log
@@ -100,7 +106,7 @@ def _kv_tiles_dense(i: int, N: int, causal: bool, kv_tile: int):
 def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hkv: int,
                       kv_idx=None, kv_cnt=None, kv_tile: int = K_BLOCK,
                       p_dtype: str | None = None, out_dtype: str | None = None,
-                      blocks=None):
+                      blocks=None, tau: float = 0.0):
     """The quantized path, step by step.
 
     q_i8 [B,Hq,N,d] int8, q_scale [B,Hq,N/128] f32, k_i8 [B,Hkv,N,d] int8,
@@ -109,7 +115,8 @@ def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hk
     64-key blocks, ascending); then ``kv_tile`` must be 64.
     ``p_dtype`` is the dtype P is rounded to ("bf16", "f16", or "f32" for no
     16-bit rounding); ``out_dtype`` the output's. Both default to V's dtype,
-    which must then be given as a torch tensor.
+    which must then be given as a torch tensor. ``tau`` is the reference
+    threshold of the online softmax (log2 units, see the module docstring).
 
     Returns (O rounded [B,Hq,N,d] f32 values, O before the final rounding
     [B,Hq,N,d] f32, lse [B,Hq,N] f64). ``blocks`` restricts the work to a list
@@ -165,7 +172,9 @@ def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hk
             s = (S.astype(np.float32) * alpha[None, :]).astype(np.float32)
             if causal:
                 s = np.where(keys[None, :] <= rows[:, None], s, ninf)
-            m_new = np.maximum(m, s.max(axis=1))
+            m_cand = np.maximum(m, s.max(axis=1))
+            move = m_cand > (m + np.float32(tau)).astype(np.float32)
+            m_new = np.where(move, m_cand, m).astype(np.float32)
             live = np.isfinite(m_new)
             arg = np.where(live[:, None], (s - np.where(live, m_new, 0)[:, None]).astype(np.float32), ninf)
             P = np.exp2(arg.astype(np.float64)).astype(np.float32)

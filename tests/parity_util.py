@@ -17,6 +17,9 @@ import oracle
 # cosine-similarity floor against exact fp64 attention.
 TOL_EMU = 2e-3
 COS_MIN = 0.999
+# the kernel's online-softmax reference threshold (QATTN_SOFTMAX_REF_THRESHOLD
+# in include/qattn.h); the emulation takes the same rule
+KERNEL_TAU = 8.0
 
 
 def log(msg: str):

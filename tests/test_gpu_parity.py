@@ -15,8 +15,8 @@ import torch
 
 import oracle
 from synthetic import make_case, make_config
-from parity_util import (TOL_EMU, COS_MIN, log, out_err, max_abs_rel, cos, to_np, run_gpu,
-                         head_slice)
+from parity_util import (TOL_EMU, COS_MIN, KERNEL_TAU, log, out_err, max_abs_rel, cos, to_np,
+                         run_gpu, head_slice)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,8 @@ def test_fwd_matches_emulation_and_exact(gpu_lib, name, kw):
     plan, o = run_gpu(gpu_lib, p, t)
     sq = oracle.smooth_quant(t["q"], t["k"])
     O_emu, O_pre, lse_emu = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
-                                                     sq["k_scale"], t["v"], p.causal, p.Hq, p.Hkv)
+                                                     sq["k_scale"], t["v"], p.causal, p.Hq, p.Hkv,
+                                                     tau=KERNEL_TAU)
     O_ex, _ = oracle.exact_attention(t["q"], t["k"], t["v"], p.causal)
     og = to_np(o)
     e = out_err(og, O_pre, p.dtype)
@@ -101,7 +102,7 @@ def test_sparse_fwd_matches_emulation(gpu_lib):
     sq = oracle.smooth_quant(t["q"], t["k"])
     O_emu, O_pre, _ = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                sq["k_scale"], t["v"], True, p.Hq, p.Hkv,
-                                               kv_idx=idx, kv_cnt=cnt)
+                                               kv_idx=idx, kv_cnt=cnt, tau=KERNEL_TAU)
     O_ex, _ = oracle.exact_attention(t["q"], t["k"], t["v"], True, idx, cnt)
     og = to_np(o)
     e, c = out_err(og, O_pre, p.dtype), cos(og, O_ex)
@@ -187,7 +188,8 @@ def _sampled_check(qa, c, n_blocks=3):
         kv_idx, kv_cnt = gi[None].astype(np.int32), gc[None].astype(np.int32)
     O_emu, O_pre, _ = oracle.emulate_attention(ref["q_i8"], ref["q_scale"], ref["k_i8"],
                                                ref["k_scale"], sub["v"], p.causal, ps.Hq, 1,
-                                               kv_idx=kv_idx, kv_cnt=kv_cnt, blocks=sel)
+                                               kv_idx=kv_idx, kv_cnt=kv_cnt, blocks=sel,
+                                               tau=KERNEL_TAU)
     O_ex, _ = oracle.exact_attention(sub["q"], sub["k"], sub["v"], p.causal, kv_idx, kv_cnt,
                                      blocks=sel)
     og = to_np(o[b, hqs])[None]

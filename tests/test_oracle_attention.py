@@ -222,3 +222,33 @@ def test_emulation_lse_matches_exact_lse_of_smoothed_logits():
     _, lse_e = exact_attention(t["q"], ks, t["v"], True)
     # quantization error of the logits, not rounding, sets this bound
     assert np.abs(lse - lse_e).max() < 0.05
+
+
+@pytest.mark.parametrize("tau", [1.0, 8.0, 20.0])
+def test_online_reference_threshold_changes_nothing_exactly(tau):
+    # with unrounded P the exponent reference cancels between acc and l: any
+    # threshold gives the single-tile (two-pass) result up to fp32 rounding
+    p, t = make_case(B=1, Hq=2, Hkv=1, N=512, d=128, dtype="bf16", causal=True, seed=15,
+                     k_offset_std=3.0, outliers=4)
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    args = (sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], t["v"], True, 2, 1)
+    _, a, la = emulate_attention(*args, p_dtype="f32", tau=tau)
+    _, b, lb = emulate_attention(*args, kv_tile=512, p_dtype="f32")
+    assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max()
+    assert np.abs(la - lb).max() < 1e-5
+    # with 16-bit P the difference is the rounding of P at other scales only
+    a16 = emulate_attention(*args, tau=tau)[1]
+    b16 = emulate_attention(*args)[1]
+    assert np.abs(a16 - b16).max() <= 2 * 2.0 ** -8 * np.abs(b16).max()
+
+
+def test_online_reference_threshold_keeps_closed_forms():
+    p, t = make_case(B=1, Hq=2, Hkv=1, N=256, d=64, dtype="bf16", causal=True, seed=16)
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    ones = torch.ones_like(t["v"])
+    O1 = emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], ones, True,
+                           2, 1, tau=8.0)[0]
+    assert np.all(O1 == 1.0)
+    O = emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], t["v"], True,
+                          2, 1, tau=8.0)[0]
+    assert np.array_equal(O[0, 0, 0], t["v"][0, 0, 0].float().numpy())
