@@ -23,10 +23,10 @@
 // conflicts. The V^T operand comes from ds_read_b64_tr_b16, which hands each
 // lane 4 consecutive keys of one channel.
 //
-// Pipeline: K is staged two tiles ahead and V one tile ahead (double buffers,
-// asynchronous loads issued at the top of an iteration and waited for at its
-// end, one barrier per tile); S of tile t+1 is computed before P V of tile t
-// so the matrix cores have independent work while the softmax of tile t runs.
+// Pipeline (triple buffers, one barrier per tile): iteration t issues the
+// asynchronous loads of K(t+3) and V(t+2), computes softmax and P V of tile t
+// and S of tile t+1, then waits only for the loads issued one iteration
+// earlier (K(t+2), V(t+1)), so every load has a full iteration to land.
 //
 // Online softmax reference: a row's exponent reference m moves only when the
 // tile's running max exceeds it by more than kTau (log2 units); otherwise P is
@@ -53,10 +53,6 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 constexpr int kKT = 64;             // keys per tile
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
 constexpr int kMaxSparseTiles = 2048;
-
-#ifndef QATTN_PINGPONG
-#define QATTN_PINGPONG 0
-#endif
 
 template <bool BF16>
 struct Mma16;
@@ -118,33 +114,45 @@ struct Geo {
   static constexpr int DB = D / 32;        // 32-row blocks of O^T
   static constexpr int KSLOTS = D / 16;    // 16-byte slots per K row
   static constexpr int VSLOTS = D / 8;     // 16-byte slots per V row
-  // swizzle of a K row: slot s of row r holds chunk s ^ kswz(r); spreads the 8
-  // rows read together (one per lane of an 8-lane phase) over all banks
-  static __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); }
-  // swizzle of a V row: the 4 rows a 16-lane transposing read touches land on
-  // disjoint 32-byte bank groups
-  static __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+  // The LDS has 64 banks of 4 bytes (256 bytes per cycle): a 16-byte read is
+  // served 16 lanes at a time, an 8-byte transposing read 32 lanes at a time.
+  // Swizzle of a K row: slot s of row r holds chunk s ^ kswz(r), so the 16
+  // consecutive rows of one 16-lane phase (same chunk) cover all 64 banks.
+  static __device__ __forceinline__ int kswz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+  // Swizzle of a V row: the 32 lanes of one phase read 4 rows x 2 channel
+  // halves x 32 bytes; these 8 pieces land on disjoint bank groups.
+  static __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
+// 16 bytes per lane from global memory straight into LDS at
+// lds_wave_base + 16 * lane (global_load_lds_dwordx4, LDS base in M0).
 __device__ __forceinline__ void lds_dma16(const void* g, int8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
   using op_t = typename MM::op_t;
   using pair_t = typename MM::pair_t;
   using el_t = typename MM::el_t;
   using G = Geo<D>;
-  constexpr int KPW = G::KBUF / 1024 / NW;  // 1 KB direct loads per wave per K tile
-  constexpr int VPW = G::VBUF / 1024 / NW;  // same for V
-  static_assert(KPW >= 1 && VPW >= 1, "tile too small for the workgroup");
-  __shared__ __attribute__((aligned(16))) int8_t k_lds[2][G::KBUF];
-  __shared__ __attribute__((aligned(16))) int8_t v_lds[2][G::VBUF];
-  __shared__ int tile_list[SPARSE ? kMaxSparseTiles : 1];
+  constexpr int RW = 32 * QB;
+  constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
+  constexpr int VPIECES = G::VBUF / 1024;
+  // three K and three V buffers as distinct objects, always named with
+  // compile-time indices: the compiler can then tell that an LDS read of one
+  // buffer does not depend on the DMA loads still landing in another, and
+  // waits only for the loads of the buffer it reads
+  __shared__ __attribute__((aligned(16))) int8_t k_lds0[G::KBUF];
+  __shared__ __attribute__((aligned(16))) int8_t k_lds1[G::KBUF];
+  __shared__ __attribute__((aligned(16))) int8_t k_lds2[G::KBUF];
+  __shared__ __attribute__((aligned(16))) int8_t v_lds0[G::VBUF];
+  __shared__ __attribute__((aligned(16))) int8_t v_lds1[G::VBUF];
+  __shared__ __attribute__((aligned(16))) int8_t v_lds2[G::VBUF];
+  __shared__ int16_t tile_list[SPARSE ? kMaxSparseTiles : 1];
   __shared__ int n_list;
 
   const int lane = threadIdx.x & 63;
@@ -163,11 +171,11 @@ void attn_fwd_kernel(FwdArgs a) {
     const int g = slot / nkvu;
     hq = (kvu % a.Hkv) * a.group + g;
     qblk = CAUSAL ? (a.nqb - 1 - rank) : rank;
-    row0 = qblk * kQBlock + 64 * wave;
+    row0 = qblk * kQBlock + RW * wave;
     wg_last_row = qblk * kQBlock + kQBlock - 1;
   } else {
     const int g4 = a.g4;
-    const int rows_wg = 64 * (NW / g4);
+    const int rows_wg = RW * (NW / g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const int nsub = a.group / g4;
     const int nslot = nkvu * nsub;
@@ -177,7 +185,7 @@ void attn_fwd_kernel(FwdArgs a) {
     const int hs = slot / nkvu;
     const int rc = CAUSAL ? (nrc - 1 - rank) : rank;
     hq = (kvu % a.Hkv) * a.group + hs * g4 + wave % g4;
-    row0 = rc * rows_wg + 64 * (wave / g4);
+    row0 = rc * rows_wg + RW * (wave / g4);
     wg_last_row = min(a.N, rc * rows_wg + rows_wg) - 1;
     qblk = row0 / kQBlock;
   }
@@ -199,7 +207,7 @@ void attn_fwd_kernel(FwdArgs a) {
         const int t = e < cnt ? src[e] : -1;
         const bool ok = t >= 0 && t < a.nkb && (!CAUSAL || t * kKT <= wg_last_row);
         const uint64_t bal = __ballot(ok);
-        if (ok) tile_list[n + __popcll(bal & lt)] = t;
+        if (ok) tile_list[n + __popcll(bal & lt)] = (int16_t)t;
         n += __popcll(bal);
       }
       if (lane == 0) n_list = n;
@@ -213,74 +221,101 @@ void attn_fwd_kernel(FwdArgs a) {
     if constexpr (SPARSE) return tile_list[it];
     else return it;
   };
-  // causal: the last tile this wave sees is its diagonal tile row0 / 64
-  auto wave_needs = [&](int t) -> bool { return wave_live && (!CAUSAL || t * kKT <= row0); };
+  // causal: a tile is needed while its first key is at or before the wave's
+  // last row; it needs masking when it reaches past the wave's first row
+  auto wave_needs = [&](int t) -> bool { return wave_live && (!CAUSAL || t * kKT <= row0 + RW - 1); };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------------
-  v4i qf[2][G::KS];
+  v4i qf[QB][G::KS];
   if (wave_live) {
     const int8_t* qg = a.q_i8 + (bhq * a.N + row0) * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks)
         qf[qb][ks] = *reinterpret_cast<const v4i*>(qg + (size_t)(32 * qb + l32) * D + 32 * ks + 16 * h);
   }
   const float alpha_q = wave_live ? a.q_scale[bhq * a.nqb + qblk] * a.c : 0.0f;
-  const float* kscale = a.k_scale + (size_t)kvu * a.nkb;
+  // k_scale through the constant address space: a uniform index makes this a
+  // scalar load (counted by lgkmcnt), so it never waits behind the in-flight
+  // vector (LDS DMA) loads of later tiles
+  const __attribute__((address_space(4))) float* kscale =
+      (const __attribute__((address_space(4))) float*)(a.k_scale + (size_t)kvu * a.nkb);
 
-  v16f acc[G::DB][2];
+  v16f acc[G::DB][QB];
 #pragma unroll
   for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.0f;
-  float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};
-  float l_run[2] = {0.0f, 0.0f};  // this lane's half of each row sum
+  float m_ref[QB], l_run[QB];  // l_run: this lane's half of the row sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = -__builtin_inff();
+    l_run[qb] = 0.0f;
+  }
 
   // ---- staging: direct global -> LDS, 1 KB per wave instruction -------------------
-  // K piece p holds rows (1024/KROW)*p ..; lane l writes slot l % KSLOTS of row
-  // l / KSLOTS, i.e. the global chunk (slot ^ kswz(row)).
-  const int k_lane_src = [&] {
-    const int r = lane / G::KSLOTS, sl = lane % G::KSLOTS;
-    return r * G::KROW + ((sl ^ G::kswz(r)) * 16);
-  }();
-  const int v_lane_src = [&] {
-    const int r = lane / G::VSLOTS, sl = lane % G::VSLOTS;
-    return r * G::VROW + ((sl ^ G::vswz(r)) * 16);
-  }();
-  auto load_k = [&](int t, int buf) {
-    const int8_t* src = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D + k_lane_src;
+  // In piece p, lane l writes slot l % SLOTS of row p*(1024/ROW) + l / SLOTS,
+  // so it fetches that row's global chunk (slot ^ swizzle(row)).
+  auto k_src_off = [&](int piece) {
+    const int r = piece * (1024 / G::KROW) + lane / G::KSLOTS;
+    return r * G::KROW + (((lane % G::KSLOTS) ^ G::kswz(r)) * 16);
+  };
+  auto v_src_off = [&](int piece) {
+    const int r = piece * (1024 / G::VROW) + lane / G::VSLOTS;
+    return r * G::VROW + (((lane % G::VSLOTS) ^ G::vswz(r)) * 16);
+  };
+  auto load_k = [&](int t, int8_t* buf) {
+    const int8_t* src = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D;
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int piece = wave + NW * j;
-      lds_dma16(src + piece * 1024, &k_lds[buf][piece * 1024]);
+    for (int piece = wave; piece < KPIECES; piece += NW)
+      lds_dma16(src + k_src_off(piece), buf + piece * 1024);
+  };
+  auto load_v = [&](int t, int8_t* buf) {
+    const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)t * kKT) * D);
+#pragma unroll
+    for (int piece = wave; piece < VPIECES; piece += NW)
+      lds_dma16(src + v_src_off(piece), buf + piece * 1024);
+  };
+  // loads one wave issues per K / V tile (the fewest over the waves: waiting
+  // for that many to remain outstanding is safe for every wave)
+  constexpr int KPW = KPIECES / NW;
+  constexpr int VPW = VPIECES / NW;
+  static_assert(VPW >= 1, "every wave stages part of each V tile");
+  auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // workgroup barrier without the compiler's implied full memory wait: the
+  // LDS DMA loads this wave still has in flight target buffers nobody reads
+  // before the next barrier, and its own LDS reads are drained here
+  auto barrier = [] {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // wait until at most `pending` of this wave's loads are in flight
+  auto wait_older = [&](bool k_pending, bool v_pending) {
+    if (k_pending && v_pending) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KPW + VPW) : "memory");
+    } else if (v_pending) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPW) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  auto load_v = [&](int t, int buf) {
-    const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)t * kKT) * D) + v_lane_src;
-#pragma unroll
-    for (int j = 0; j < VPW; ++j) {
-      const int piece = wave + NW * j;
-      lds_dma16(src + piece * 1024, &v_lds[buf][piece * 1024]);
-    }
-  };
-  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- compute helpers -----------------------------------------------------------
-  // K fragment (key row kb*32 + l32, chunk 2*ks + h), swizzled; kb*32 keeps kswz
+  // K fragment (key row kb*32 + l32, chunk 2*ks + h), swizzled; kswz only
+  // depends on the row's low five bits, so kb*32 keeps it
   int k_frag_off[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
-  auto qk = [&](int buf, v16i (&s)[2][2]) {
+  auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const v4i kf = *reinterpret_cast<const v4i*>(&k_lds[buf][kb * 32 * G::KROW + k_frag_off[ks]]);
+        const v4i kf = *reinterpret_cast<const v4i*>(kbuf + kb * 32 * G::KROW + k_frag_off[ks]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           if (ks == 0) {
             const v16i zero = {};
             s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], zero, 0, 0, 0);
@@ -294,11 +329,11 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // softmax of one tile, one 32-query block at a time: S (exact int32) -> P
   // packed in the B-operand layout of the P V product
-  auto softmax = [&](const v16i (&s)[2][2], int t, op_t (&pf)[2][2][2]) {
-    const float alpha = alpha_q * kscale[t];
-    const bool diag = CAUSAL && t * kKT == row0;
+  auto softmax = [&](const v16i (&s)[2][QB], int t, op_t (&pf)[2][QB][2]) {
+    const float alpha = alpha_q * kscale[__builtin_amdgcn_readfirstlane(t)];
+    const bool diag = CAUSAL && t * kKT + kKT - 1 > row0;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float f[2][16];
       float mx = -__builtin_inff();
 #pragma unroll
@@ -307,8 +342,8 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           float x = (float)s[kb][qb][r];
           if (diag) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > 32 * qb + l32) x = -__builtin_inff();
+            const int key = t * kKT + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > row0 + 32 * qb + l32) x = -__builtin_inff();
           }
           f[kb][r] = x;
           mx = __builtin_fmaxf(mx, x);
@@ -351,8 +386,8 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // transposing V reads: 16-lane group g = lane/16 reads key rows
   // k0 + 4*(g/2) + (lane%16)/4 and the 32 bytes of channels
-  // 32*db + 16*(g%2) + [0, 16); lane j of the group takes 8 of them. The row's
-  // low two bits (the swizzle input) depend on the lane only.
+  // 32*db + 16*(g%2) + [0, 16); lane j of the group takes 8 of them. k0 is a
+  // multiple of 8, so the row bits the swizzle reads depend on the lane only.
   const int grp = lane >> 4;
   const int vr_lane = 4 * (grp >> 1) + ((lane >> 2) & 3);
   int v_frag_off[G::DB];
@@ -361,75 +396,64 @@ void attn_fwd_kernel(FwdArgs a) {
     const int slot = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
     v_frag_off[db] = vr_lane * G::VROW + ((slot ^ G::vswz(vr_lane)) * 16) + 8 * (lane & 1);
   }
-  auto pv = [&](int buf, const op_t (&pf)[2][2][2]) {
+  auto pv = [&](const int8_t* vbuf, const op_t (&pf)[2][QB][2]) {
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int8_t* p = &v_lds[buf][(kb * 32 + 16 * half) * G::VROW + v_frag_off[db]];
+          const int8_t* p = vbuf + (kb * 32 + 16 * half) * G::VROW + v_frag_off[db];
           const v4s lo = lds_read_tr16(p);
           const v4s hi = lds_read_tr16(p + 8 * G::VROW);
           const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const op_t vf = __builtin_bit_cast(op_t, both);
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) acc[db][qb] = MM::mma(vf, pf[kb][qb][half], acc[db][qb]);
+          for (int qb = 0; qb < QB; ++qb) acc[db][qb] = MM::mma(vf, pf[kb][qb][half], acc[db][qb]);
         }
   };
 
   // ---- pipeline ---------------------------------------------------------------------
-  if (ntiles > 0) {
-    load_k(tile_of(0), 0);
-    load_v(tile_of(0), 0);
-    if (ntiles > 1) load_k(tile_of(1), 1);
-  }
-  wait_loads();
+  if (ntiles > 0) load_k(tile_of(0), k_lds0);
+  if (ntiles > 1) load_k(tile_of(1), k_lds1);
+  if (ntiles > 2) load_k(tile_of(2), k_lds2);
+  if (ntiles > 0) load_v(tile_of(0), v_lds0);
+  if (ntiles > 1) load_v(tile_of(1), v_lds1);
+  wait_all();
   __syncthreads();
 
-  v16i s_a[2][2], s_b[2][2];
-  if (ntiles > 0 && wave_needs(tile_of(0))) qk(0, s_a);
-
-  auto step = [&](int it, v16i (&s_cur)[2][2], v16i (&s_nxt)[2][2]) {
+  v16i s[2][QB];
+  if (ntiles > 0 && wave_needs(tile_of(0))) qk(k_lds0, s);
+  // one tile; K(it), V(it-1) were last read before the previous barrier, so
+  // their buffers (it % 3 == (it+3) % 3, (it+2) % 3) take K(it+3) and V(it+2)
+  auto step = [&](int it, int8_t* k_cur, int8_t* k_next, int8_t* v_cur, int8_t* v_after) {
     const int t = tile_of(it);
-    const bool pre_k = it + 2 < ntiles;
-    const bool pre_v = it + 1 < ntiles;
-    // K(it) and V(it-1) were consumed before the last barrier: their buffers
-    // take K(it+2) and V(it+1)
-    if (pre_k) load_k(tile_of(it + 2), it & 1);
-    if (pre_v) load_v(tile_of(it + 1), (it + 1) & 1);
-    const bool cur = wave_needs(t);
-    const bool nxt = pre_v && wave_needs(tile_of(it + 1));
-    op_t pf[2][2][2];
-#if QATTN_PINGPONG
-    if (cur) softmax(s_cur, t, pf);
-    if (nxt) qk((it + 1) & 1, s_nxt);
-    if (cur) pv(it & 1, pf);
-#else
-    if (cur) {
-      softmax(s_cur, t, pf);
-      pv(it & 1, pf);
+    const bool pre_k = it + 3 < ntiles;
+    const bool pre_v = it + 2 < ntiles;
+    if (pre_k) load_k(tile_of(it + 3), k_cur);
+    if (pre_v) load_v(tile_of(it + 2), v_after);
+    if (wave_needs(t)) {
+      op_t pf[2][QB][2];
+      softmax(s, t, pf);
+      pv(v_cur, pf);
     }
-    if (nxt) qk((it + 1) & 1, s_cur);
-    (void)s_nxt;
-#endif
-    wait_loads();
-    __syncthreads();
+    if (it + 1 < ntiles && wave_needs(tile_of(it + 1))) qk(k_next, s);
+    wait_older(pre_k, pre_v);
+    barrier();
   };
-
   int it = 0;
-#if QATTN_PINGPONG
-  for (; it + 1 < ntiles; it += 2) {
-    step(it, s_a, s_b);
-    step(it + 1, s_b, s_a);
+  for (; it + 3 <= ntiles; it += 3) {
+    step(it, k_lds0, k_lds1, v_lds0, v_lds2);
+    step(it + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+    step(it + 2, k_lds2, k_lds0, v_lds2, v_lds1);
   }
-#endif
-  for (; it < ntiles; ++it) step(it, s_a, s_b);
+  if (it < ntiles) step(it, k_lds0, k_lds1, v_lds0, v_lds2);
+  if (it + 1 < ntiles) step(it + 1, k_lds1, k_lds2, v_lds1, v_lds0);
 
   // ---- epilogue: O = acc / l, lse --------------------------------------------------
   if (!wave_live) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int q = row0 + 32 * qb + l32;
@@ -456,16 +480,29 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+#ifndef QATTN_NW_DENSE
+#define QATTN_NW_DENSE 4
+#endif
+#ifndef QATTN_QB
+#define QATTN_QB 1
+#endif
+
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
+  constexpr int QB = QATTN_QB;          // 32-query blocks per wave
+  constexpr int WPE = QB == 1 ? 2 : 1;  // waves per SIMD
+  constexpr int NW_DENSE = QATTN_NW_DENSE;
+  constexpr int NW_SPARSE = 128 / (32 * QB);
   if (sparse) {
     const dim3 grid(a.B * a.Hq * a.nqb);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, WPE>), grid,
+                       dim3(NW_SPARSE * 64), 0, stream, a);
   } else {
-    const int rows_wg = 64 * (4 / a.g4);
+    const int rows_wg = 32 * QB * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, 4>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE>), grid,
+                       dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();
 }
