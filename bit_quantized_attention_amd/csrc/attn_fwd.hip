@@ -24,9 +24,10 @@
 // lane 4 consecutive keys of one channel.
 //
 // Pipeline (triple buffers, one barrier per tile): iteration t issues the
-// asynchronous loads of K(t+3) and V(t+2), computes softmax and P V of tile t
-// and S of tile t+1, then waits only for the loads issued one iteration
-// earlier (K(t+2), V(t+1)), so every load has a full iteration to land.
+// asynchronous loads of V(t+1) and K(t+3), computes the softmax of tile t, a
+// P V product and S of tile t+1, then waits for everything but its K loads.
+// In 8-wave workgroups the waves sharing a SIMD take opposite ping-pong roles
+// (see the pipeline below) so that VALU and matrix work overlap.
 //
 // Online softmax reference: a row's exponent reference m moves only when the
 // tile's running max exceeds it by more than kTau (log2 units); otherwise P is
@@ -282,8 +283,6 @@ void attn_fwd_kernel(FwdArgs a) {
   // loads one wave issues per K / V tile (the fewest over the waves: waiting
   // for that many to remain outstanding is safe for every wave)
   constexpr int KPW = KPIECES / NW;
-  constexpr int VPW = VPIECES / NW;
-  static_assert(VPW >= 1, "every wave stages part of each V tile");
   auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   // workgroup barrier without the compiler's implied full memory wait: the
   // LDS DMA loads this wave still has in flight target buffers nobody reads
@@ -291,12 +290,11 @@ void attn_fwd_kernel(FwdArgs a) {
   auto barrier = [] {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  // wait until at most `pending` of this wave's loads are in flight
-  auto wait_older = [&](bool k_pending, bool v_pending) {
-    if (k_pending && v_pending) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KPW + VPW) : "memory");
-    } else if (v_pending) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(VPW) : "memory");
+  // wait for every load of this wave except this iteration's K loads (issued
+  // last) when there are some
+  auto wait_older = [&](bool k_pending, bool) {
+    if (k_pending && KPW > 0) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KPW) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -308,6 +306,13 @@ void attn_fwd_kernel(FwdArgs a) {
   int k_frag_off[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
+  // S is accumulated on top of the integer bit pattern of kMagic = 1.5 * 2^23:
+  // the int32 result M + S read as a float is exactly kMagic + S (|S| <=
+  // 128 * 127^2 < 2^22), so the softmax gets floats without a conversion and
+  // recovers S exactly with one subtraction.
+  v16i magic;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) magic[r] = 0x4B400000;
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
@@ -317,8 +322,7 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (ks == 0) {
-            const v16i zero = {};
-            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], zero, 0, 0, 0);
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], magic, 0, 0, 0);
           } else {
             s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
           }
@@ -327,29 +331,50 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // softmax of one tile, one 32-query block at a time: S (exact int32) -> P
-  // packed in the B-operand layout of the P V product
+  // softmax of one tile, one 32-query block at a time: S (kMagic-biased
+  // floats) -> P packed in the B-operand layout of the P V product
+  constexpr float kMagic = 12582912.0f;
   auto softmax = [&](const v16i (&s)[2][QB], int t, op_t (&pf)[2][QB][2]) {
     const float alpha = alpha_q * kscale[__builtin_amdgcn_readfirstlane(t)];
     const bool diag = CAUSAL && t * kKT + kKT - 1 > row0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float f[2][16];
-      float mx = -__builtin_inff();
+      float f[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = (float)s[kb][qb][r];
-          if (diag) {
-            const int key = t * kKT + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > row0 + 32 * qb + l32) x = -__builtin_inff();
-          }
-          f[kb][r] = x;
-          mx = __builtin_fmaxf(mx, x);
+          // copy the element out first: __builtin_bit_cast of a vector
+          // element reads the vector's first element
+          const int si = s[kb][qb][r];
+          f[16 * kb + r] = __builtin_bit_cast(float, si);
         }
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mc = __builtin_fmaxf(m_ref[qb], mx * alpha);
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t * kKT + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > row0 + 32 * qb + l32) f[16 * kb + r] = -__builtin_inff();
+          }
+      }
+      // row max: a max3 tree over the lane's 32 keys, then the other half-row
+      float m8[11];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) m8[j] = __builtin_fmaxf(__builtin_fmaxf(f[3 * j], f[3 * j + 1]), f[3 * j + 2]);
+      m8[10] = __builtin_fmaxf(f[30], f[31]);
+      const float m4a = __builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), m8[2]);
+      const float m4b = __builtin_fmaxf(__builtin_fmaxf(m8[3], m8[4]), m8[5]);
+      const float m4c = __builtin_fmaxf(__builtin_fmaxf(m8[6], m8[7]), m8[8]);
+      const float m4d = __builtin_fmaxf(m8[9], m8[10]);
+      float mx = __builtin_fmaxf(__builtin_fmaxf(m4a, m4b), __builtin_fmaxf(m4c, m4d));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mx),
+                                                         __builtin_bit_cast(int, mx), false, false);
+        mx = __builtin_fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+      }
+      // fl32(max S * alpha): the subtraction is exact (same binade)
+      const float mc = __builtin_fmaxf(m_ref[qb], (mx - kMagic) * alpha);
       const bool move = mc > m_ref[qb] + kTau;
       if (__ballot(move) != 0) {
         float corr = 1.0f;
@@ -364,23 +389,26 @@ void attn_fwd_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr;
       }
       const float m_use = (m_ref[qb] == -__builtin_inff()) ? 0.0f : m_ref[qb];
-      float lsum = 0.0f;
+      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           op_t pk;
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pk[e] = (el_t)__builtin_amdgcn_exp2f(__builtin_fmaf(f[kb][8 * half + e], alpha, -m_use));
+          for (int e = 0; e < 8; ++e) {
+            const float d = f[16 * kb + 8 * half + e] - kMagic;  // exact: S as a float
+            pk[e] = (el_t)__builtin_amdgcn_exp2f(__builtin_fmaf(d, alpha, -m_use));
+          }
+          // four independent fp32 partial sums of the rounded P
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const pair_t pr = {pk[e], pk[e + 1]};
-            lsum = MM::sum2(pr, lsum);
+          for (int w = 0; w < 4; ++w) {
+            const pair_t pr = {pk[2 * w], pk[2 * w + 1]};
+            lsum[w] = MM::sum2(pr, lsum[w]);
           }
           pf[kb][qb][half] = pk;
         }
-      l_run[qb] += lsum;
+      l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     }
   };
 
@@ -414,41 +442,71 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // ---- pipeline ---------------------------------------------------------------------
+  if (ntiles > 0) load_v(tile_of(0), v_lds0);
   if (ntiles > 0) load_k(tile_of(0), k_lds0);
   if (ntiles > 1) load_k(tile_of(1), k_lds1);
   if (ntiles > 2) load_k(tile_of(2), k_lds2);
-  if (ntiles > 0) load_v(tile_of(0), v_lds0);
-  if (ntiles > 1) load_v(tile_of(1), v_lds1);
   wait_all();
   __syncthreads();
 
+  // Ping-pong roles (dense, 8 waves: waves w and w+4 share a SIMD). Role A
+  // runs softmax(t), P V(t), S(t+1); role B runs P V(t-1), softmax(t), S(t+1),
+  // so on each SIMD one wave's softmax (VALU) runs against the other's matrix
+  // products. B keeps P(t-1) across the barrier and finishes with P V(last).
+  constexpr bool kPingPong = !SPARSE && NW == 8;
+  const bool role_b = kPingPong && wave >= 4;
+
   v16i s[2][QB];
+  op_t p_prev[2][QB][2];
+  bool have_prev = false;
   if (ntiles > 0 && wave_needs(tile_of(0))) qk(k_lds0, s);
-  // one tile; K(it), V(it-1) were last read before the previous barrier, so
-  // their buffers (it % 3 == (it+3) % 3, (it+2) % 3) take K(it+3) and V(it+2)
-  auto step = [&](int it, int8_t* k_cur, int8_t* k_next, int8_t* v_cur, int8_t* v_after) {
+  // one tile. Buffers: tile j's K and V live in buffer j % 3. The loads of
+  // iteration it go to V(it+1) -> (it+1) % 3 (last read by role B at it-1)
+  // and K(it+3) -> it % 3 (K(it) was last read at it-1); V is issued first so
+  // that waiting for it leaves only this iteration's K loads in flight.
+  auto step = [&](int it, int8_t* k_cur, int8_t* k_next, const int8_t* v_prev,
+                  const int8_t* v_cur, int8_t* v_next) {
     const int t = tile_of(it);
+    const bool pre_v = it + 1 < ntiles;
     const bool pre_k = it + 3 < ntiles;
-    const bool pre_v = it + 2 < ntiles;
+    if (pre_v) load_v(tile_of(it + 1), v_next);
     if (pre_k) load_k(tile_of(it + 3), k_cur);
-    if (pre_v) load_v(tile_of(it + 2), v_after);
-    if (wave_needs(t)) {
+    const bool need = wave_needs(t);
+    if (role_b) {
+      if (have_prev) pv(v_prev, p_prev);
+      op_t pf[2][QB][2];
+      if (need) softmax(s, t, pf);
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < QB; ++y)
+#pragma unroll
+          for (int z = 0; z < 2; ++z) p_prev[x][y][z] = pf[x][y][z];
+      have_prev = need;
+    } else if (need) {
       op_t pf[2][QB][2];
       softmax(s, t, pf);
       pv(v_cur, pf);
     }
     if (it + 1 < ntiles && wave_needs(tile_of(it + 1))) qk(k_next, s);
-    wait_older(pre_k, pre_v);
+    wait_older(pre_k, false);
     barrier();
   };
   int it = 0;
   for (; it + 3 <= ntiles; it += 3) {
-    step(it, k_lds0, k_lds1, v_lds0, v_lds2);
-    step(it + 1, k_lds1, k_lds2, v_lds1, v_lds0);
-    step(it + 2, k_lds2, k_lds0, v_lds2, v_lds1);
+    step(it, k_lds0, k_lds1, v_lds2, v_lds0, v_lds1);
+    step(it + 1, k_lds1, k_lds2, v_lds0, v_lds1, v_lds2);
+    step(it + 2, k_lds2, k_lds0, v_lds1, v_lds2, v_lds0);
   }
-  if (it < ntiles) step(it, k_lds0, k_lds1, v_lds0, v_lds2);
-  if (it + 1 < ntiles) step(it + 1, k_lds1, k_lds2, v_lds1, v_lds0);
+  if (it < ntiles) step(it, k_lds0, k_lds1, v_lds2, v_lds0, v_lds1);
+  if (it + 1 < ntiles) step(it + 1, k_lds1, k_lds2, v_lds0, v_lds1, v_lds2);
+  if (have_prev) {
+    // role B: the last tile's P V; its V buffer is (ntiles - 1) % 3
+    const int lb = (ntiles - 1) % 3;
+    if (lb == 0) pv(v_lds0, p_prev);
+    else if (lb == 1) pv(v_lds1, p_prev);
+    else pv(v_lds2, p_prev);
+  }
 
   // ---- epilogue: O = acc / l, lse --------------------------------------------------
   if (!wave_live) return;
@@ -481,7 +539,7 @@ void attn_fwd_kernel(FwdArgs a) {
 }
 
 #ifndef QATTN_NW_DENSE
-#define QATTN_NW_DENSE 4
+#define QATTN_NW_DENSE 8
 #endif
 #ifndef QATTN_QB
 #define QATTN_QB 1
