@@ -36,6 +36,49 @@ PEAK_BF16_TFLOPS = 2500.0     # dense FP16/BF16 matrix peak
 PEAK_HBM_GBS = 8000.0
 
 
+# file-name slugs of the workloads (profile summaries are named after them)
+SLUG = {1: "tiny_noncausal_n256", 2: "llama8b_causal_n8192", 3: "vision_noncausal_n4096",
+        4: "llama8b_causal_n65536", 5: "sparse_causal_n32768"}
+KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_attention_amd", "csrc", "attn_fwd.hip")
+
+
+def counted_traffic(cfg: int):
+    """HBM-side bytes per attn_fwd launch from the committed counter summary of
+    this workload (profiles/attn_fwd_<slug>_traffic.txt): FETCH_SIZE and
+    WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain
+    copy of known size. None when there is no summary or when the kernel source
+    has changed since the counters were taken (its sha256 is recorded)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{SLUG[cfg]}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int, reps: int):
+    """A plain device copy of known size, run under rocprofv3 --pmc to calibrate
+    FETCH_SIZE / WRITE_SIZE (each launch reads and writes mib MiB)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,6 +88,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -135,6 +180,9 @@ def main():
                           "n_gpus": args.gpus}))
         print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
     import torch
     import bit_quantized_attention_amd as qa
     from synthetic import make_config
@@ -206,7 +254,7 @@ def main():
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_INT8_TOPS,
-            "traffic": None,
+            "traffic": counted_traffic(args.config),
             "kernel": "attn_fwd",
             "algorithmic_ops_per_launch": alg,
             "avg_launch_ms": fwd_avg,

@@ -28,6 +28,9 @@ QATTN_BF16 = 1
 Q_BLOCK = 128
 K_BLOCK = 64
 KV_TILE = 64
+# the attention kernel's online-softmax reference threshold
+# (QATTN_SOFTMAX_REF_THRESHOLD in include/qattn.h)
+SOFTMAX_REF_THRESHOLD = 8
 
 _STATUS = {0: "QATTN_OK", 1: "QATTN_ERR_NULL", 2: "QATTN_ERR_SHAPE", 3: "QATTN_ERR_ALIGN",
            4: "QATTN_ERR_UNSUPPORTED", 5: "QATTN_ERR_ARG", 6: "QATTN_ERR_DEVICE"}

@@ -10,6 +10,7 @@ import time
 import numpy as np
 import torch
 
+import bit_quantized_attention_amd as qa
 import oracle
 
 # Output tolerance of the quantized path against its emulation (max-abs-relative
@@ -17,9 +18,8 @@ import oracle
 # cosine-similarity floor against exact fp64 attention.
 TOL_EMU = 2e-3
 COS_MIN = 0.999
-# the kernel's online-softmax reference threshold (QATTN_SOFTMAX_REF_THRESHOLD
-# in include/qattn.h); the emulation takes the same rule
-KERNEL_TAU = 8.0
+# the kernel's online-softmax reference threshold; the emulation takes the same rule
+KERNEL_TAU = float(qa.SOFTMAX_REF_THRESHOLD)
 
 
 def log(msg: str):

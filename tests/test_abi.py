@@ -169,3 +169,12 @@ def test_load_fails_loudly_without_library(tmp_path):
             qa.load(str(tmp_path / "missing.so"))
     finally:
         qa._lib = saved
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(QATTN_[A-Z_]+)\s+(\d+)", text))
+    assert int(defs["QATTN_Q_BLOCK"]) == qa.Q_BLOCK
+    assert int(defs["QATTN_K_BLOCK"]) == qa.K_BLOCK
+    assert int(defs["QATTN_KV_TILE"]) == qa.KV_TILE
+    assert int(defs["QATTN_SOFTMAX_REF_THRESHOLD"]) == qa.SOFTMAX_REF_THRESHOLD
