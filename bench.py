@@ -39,16 +39,31 @@ PEAK_HBM_GBS = 8000.0
 # file-name slugs of the workloads (profile summaries are named after them)
 SLUG = {1: "tiny_noncausal_n256", 2: "llama8b_causal_n8192", 3: "vision_noncausal_n4096",
         4: "llama8b_causal_n65536", 5: "sparse_causal_n32768"}
-KERNEL_SOURCE = os.path.join(ROOT, "bit_quantized_attention_amd", "csrc", "attn_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_attention_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "device_util.h", "qattn_internal.h")] + \
+                 [os.path.join(ROOT, "include", "qattn.h")]
+
+
+def kernel_code_hash() -> str:
+    """sha256 over the attention kernel's sources with comments and blank space
+    removed: it changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+    return h.hexdigest()
 
 
 def counted_traffic(cfg: int):
     """HBM-side bytes per attn_fwd launch from the committed counter summary of
     this workload (profiles/attn_fwd_<slug>_traffic.txt): FETCH_SIZE and
     WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain
-    copy of known size. None when there is no summary or when the kernel source
-    has changed since the counters were taken (its sha256 is recorded)."""
-    import hashlib
+    copy of known size. None when there is no summary or when the kernel code
+    has changed since the counters were taken (its hash is recorded)."""
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{SLUG[cfg]}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -57,8 +72,7 @@ def counted_traffic(cfg: int):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != sha:
+    if kv.get("kernel_code_sha256") != kernel_code_hash():
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])

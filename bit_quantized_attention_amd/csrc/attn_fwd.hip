@@ -1,16 +1,18 @@
 // Quantized attention forward on gfx950 matrix cores.
 //
-// Work decomposition. A wave owns 64 query rows of one query head (two
-// 32-column MFMA blocks). Dense: a workgroup of 4 waves takes g4 = gcd(group,4)
-// query heads of one kv head times 4/g4 row chunks, so the 4 waves share every
-// K/V tile they stage (for GQA group 4: four heads, the same 64 rows). Sparse:
-// a workgroup of 2 waves takes one 128-row query block of one head (its kept
-// list is the workgroup's tile list). Consecutive workgroups map to distinct
-// kv heads, so blockIdx % 8 (the XCD) keeps each kv head on one XCD's L2;
-// under causal masking the longest rows are dispatched first.
+// Work decomposition. A wave owns 32 query rows of one query head (one
+// 32-column MFMA block). Dense: a workgroup of 8 waves takes g4 = 4, 2 or 1
+// query heads of one kv head (the largest that divides the group size) times
+// 8/g4 consecutive 32-row slabs, so all 8 waves share every K/V tile they
+// stage (GQA group 4: four heads x the same 64 rows). Sparse: a workgroup of
+// 4 waves takes one 128-row query block of one head; its kept list is the
+// workgroup's tile list. Consecutive workgroups map to distinct kv heads, so
+// blockIdx % 8 (the XCD) keeps each kv head on one XCD's L2; under causal
+// masking the longest rows are dispatched first.
 //
 // Per 64-key tile (registers except the K/V staging):
-//   S^T[key][q] = K_tile . Q^T       v_mfma_i32_32x32x32_i8, 2x2 blocks, 4/2 k-steps
+//   S^T[key][q] = K_tile . Q^T       v_mfma_i32_32x32x32_i8, two 32-key blocks,
+//                                    4 (d = 128) or 2 (d = 64) k-steps
 //   online base-2 softmax on S^T     lane = query column; lanes l, l+32 hold the
 //                                    two halves of its 32 keys per block
 //   O^T[d][q] += V^T . P^T           v_mfma_f32_32x32x16_{bf16,f16}
