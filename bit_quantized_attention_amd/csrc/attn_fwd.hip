@@ -25,17 +25,20 @@
 // conflicts. The V^T operand comes from ds_read_b64_tr_b16, which hands each
 // lane 4 consecutive keys of one channel.
 //
-// Pipeline (triple buffers, one barrier per tile): iteration t issues the
-// asynchronous loads of V(t+1) and K(t+3), computes the softmax of tile t, a
-// P V product and S of tile t+1, then waits for everything but its K loads.
-// In 8-wave workgroups the waves sharing a SIMD take opposite ping-pong roles
-// (see the pipeline below) so that VALU and matrix work overlap.
+// Pipeline (three K/V buffers, one barrier per tile): each wave runs S, the
+// softmax and P V of its tile in sequence; the waves sharing a SIMD overlap
+// each other's matrix and vector work. The loads of the tile two ahead go out
+// once the current S products are queued. Dense workgroups keep each wave's Q
+// fragments in LDS; every K tile carries its scale in a small tail of its LDS
+// buffer (no scalar loads in the loop).
 //
 // Online softmax reference: a row's exponent reference m moves only when the
 // tile's running max exceeds it by more than kTau (log2 units); otherwise P is
 // taken against the stale reference (P <= 2^kTau) and the accumulator is not
 // rescaled. The move test is wave-uniform, so the rescale is skipped for the
 // whole wave in the common case.
+#include <type_traits>
+
 #include "../../include/qattn.h"
 #include "device_util.h"
 #include "qattn_internal.h"
@@ -129,12 +132,27 @@ struct Geo {
 
 // 16 bytes per lane from global memory straight into LDS at
 // lds_wave_base + 16 * lane (global_load_lds_dwordx4, LDS base in M0).
+// 4 bytes per lane (global_load_lds_dword), LDS destination lds_base + 4 * lane
+__device__ __forceinline__ void lds_dma4(const void* g, int8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+}
+
 __device__ __forceinline__ void lds_dma16(const void* g, int8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE>
+// compile-time loop: f(integral_constant<int, I>) for I in [I0, N)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
@@ -145,27 +163,52 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int RW = 32 * QB;
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
-  // three K and three V buffers as distinct objects, always named with
+  // NBUF K and NBUF V buffers as distinct objects, always named with
   // compile-time indices: the compiler can then tell that an LDS read of one
   // buffer does not depend on the DMA loads still landing in another, and
   // waits only for the loads of the buffer it reads
-  __shared__ __attribute__((aligned(16))) int8_t k_lds0[G::KBUF];
-  __shared__ __attribute__((aligned(16))) int8_t k_lds1[G::KBUF];
-  __shared__ __attribute__((aligned(16))) int8_t k_lds2[G::KBUF];
+  static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
+  __shared__ __attribute__((aligned(16))) int8_t k_lds0[G::KBUF + 256];
+  __shared__ __attribute__((aligned(16))) int8_t k_lds1[G::KBUF + 256];
+  __shared__ __attribute__((aligned(16))) int8_t k_lds2[G::KBUF + 256];
+  __shared__ __attribute__((aligned(16))) int8_t k_lds3[NBUF == 4 ? G::KBUF + 256 : 16];
   __shared__ __attribute__((aligned(16))) int8_t v_lds0[G::VBUF];
   __shared__ __attribute__((aligned(16))) int8_t v_lds1[G::VBUF];
   __shared__ __attribute__((aligned(16))) int8_t v_lds2[G::VBUF];
+  __shared__ __attribute__((aligned(16))) int8_t v_lds3[NBUF == 4 ? G::VBUF : 16];
+  auto kbuf = [&](auto i) -> int8_t* {
+    constexpr int j = decltype(i)::value % NBUF;
+    if constexpr (j == 0) return k_lds0;
+    else if constexpr (j == 1) return k_lds1;
+    else if constexpr (j == 2) return k_lds2;
+    else return k_lds3;
+  };
+  auto vbuf = [&](auto i) -> int8_t* {
+    constexpr int j = decltype(i)::value % NBUF;
+    if constexpr (j == 0) return v_lds0;
+    else if constexpr (j == 1) return v_lds1;
+    else if constexpr (j == 2) return v_lds2;
+    else return v_lds3;
+  };
+  // Dense workgroups keep each wave's Q fragments in LDS (same swizzle as a
+  // K block) and read them per tile: that frees the 16 registers they would
+  // hold for the whole kernel. Sparse workgroups keep them in registers (their
+  // LDS budget allows two workgroups per CU).
+  constexpr bool QL = !SPARSE;
+  static_assert(!QL || QB == 1, "Q in LDS takes one 32-row block per wave");
+  __shared__ __attribute__((aligned(16))) int8_t q_lds[QL ? NW * 32 * D : 16];
   __shared__ int16_t tile_list[SPARSE ? kMaxSparseTiles : 1];
-  __shared__ int n_list;
+  __shared__ int n_list, n_list_plain;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a uniform (scalar) value: branches on it stay uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int nkvu = a.B * a.Hkv;
 
   // ---- work item ---------------------------------------------------------------
-  int kvu, hq, row0, wg_last_row, qblk;
+  int kvu, hq, row0, wg_row0, wg_last_row, qblk;
   if constexpr (SPARSE) {
     const int nheads = a.B * a.Hq;
     const int slot = blockIdx.x % nheads;
@@ -175,6 +218,7 @@ void attn_fwd_kernel(FwdArgs a) {
     hq = (kvu % a.Hkv) * a.group + g;
     qblk = CAUSAL ? (a.nqb - 1 - rank) : rank;
     row0 = qblk * kQBlock + RW * wave;
+    wg_row0 = qblk * kQBlock;
     wg_last_row = qblk * kQBlock + kQBlock - 1;
   } else {
     const int g4 = a.g4;
@@ -189,6 +233,7 @@ void attn_fwd_kernel(FwdArgs a) {
     const int rc = CAUSAL ? (nrc - 1 - rank) : rank;
     hq = (kvu % a.Hkv) * a.group + hs * g4 + wave % g4;
     row0 = rc * rows_wg + RW * (wave / g4);
+    wg_row0 = rc * rows_wg;
     wg_last_row = min(a.N, rc * rows_wg + rows_wg) - 1;
     qblk = row0 / kQBlock;
   }
@@ -198,35 +243,43 @@ void attn_fwd_kernel(FwdArgs a) {
   const size_t kv_row0 = (size_t)kvu * a.N;
 
   // ---- tile list -----------------------------------------------------------------
-  int ntiles;
+  // Under causal masking a tile needs the per-element mask when its last key
+  // lies past the workgroup's first row. Those tiles come last: n_plain
+  // unmasked tiles, then the masked ones (for a valid kept list, which is
+  // ascending, this is the given order).
+  auto masked = [&](int t) -> bool { return CAUSAL && t * kKT + kKT - 1 > wg_row0; };
+  int ntiles, n_plain;
   if constexpr (SPARSE) {
     if (wave == 0) {
       const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       int n = 0;
-      for (int e0 = 0; e0 < cnt; e0 += 64) {
-        const int e = e0 + lane;
-        const int t = e < cnt ? src[e] : -1;
-        const bool ok = t >= 0 && t < a.nkb && (!CAUSAL || t * kKT <= wg_last_row);
-        const uint64_t bal = __ballot(ok);
-        if (ok) tile_list[n + __popcll(bal & lt)] = (int16_t)t;
-        n += __popcll(bal);
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int e0 = 0; e0 < cnt; e0 += 64) {
+          const int e = e0 + lane;
+          const int t = e < cnt ? src[e] : -1;
+          const bool ok = t >= 0 && t < a.nkb && (!CAUSAL || t * kKT <= wg_last_row) &&
+                          (masked(t) == (pass == 1));
+          const uint64_t bal = __ballot(ok);
+          if (ok) tile_list[n + __popcll(bal & lt)] = (int16_t)t;
+          n += __popcll(bal);
+        }
+        if (pass == 0 && lane == 0) n_list_plain = n;
       }
       if (lane == 0) n_list = n;
     }
     __syncthreads();
     ntiles = n_list;
+    n_plain = n_list_plain;
   } else {
     ntiles = CAUSAL ? wg_last_row / kKT + 1 : a.nkb;
+    n_plain = CAUSAL ? min(ntiles, (wg_row0 + 1) / kKT) : ntiles;
   }
   auto tile_of = [&](int it) -> int {
     if constexpr (SPARSE) return tile_list[it];
     else return it;
   };
-  // causal: a tile is needed while its first key is at or before the wave's
-  // last row; it needs masking when it reaches past the wave's first row
-  auto wave_needs = [&](int t) -> bool { return wave_live && (!CAUSAL || t * kKT <= row0 + RW - 1); };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------------
   v4i qf[QB][G::KS];
@@ -239,11 +292,7 @@ void attn_fwd_kernel(FwdArgs a) {
         qf[qb][ks] = *reinterpret_cast<const v4i*>(qg + (size_t)(32 * qb + l32) * D + 32 * ks + 16 * h);
   }
   const float alpha_q = wave_live ? a.q_scale[bhq * a.nqb + qblk] * a.c : 0.0f;
-  // k_scale through the constant address space: a uniform index makes this a
-  // scalar load (counted by lgkmcnt), so it never waits behind the in-flight
-  // vector (LDS DMA) loads of later tiles
-  const __attribute__((address_space(4))) float* kscale =
-      (const __attribute__((address_space(4))) float*)(a.k_scale + (size_t)kvu * a.nkb);
+  const float* kscale = a.k_scale + (size_t)kvu * a.nkb;
 
   v16f acc[G::DB][QB];
 #pragma unroll
@@ -270,36 +319,49 @@ void attn_fwd_kernel(FwdArgs a) {
     const int r = piece * (1024 / G::VROW) + lane / G::VSLOTS;
     return r * G::VROW + (((lane % G::VSLOTS) ^ G::vswz(r)) * 16);
   };
+  // Every wave issues the same fixed number of 1 KB loads per tile (KPW, VPW):
+  // piece (wave + NW*j) % PIECES. When a tile has fewer pieces than the group
+  // has waves, several waves load the same piece (identical bytes).
+  // wave w loads pieces w, w+NW, ... (mod the piece count): every piece is
+  // covered, and a few are loaded twice (identical bytes) when the piece count
+  // is not a multiple of the wave count
+  constexpr int KPW = (KPIECES + NW - 1) / NW;
+  constexpr int VPW = (VPIECES + NW - 1) / NW;
+  // The K tile's scale rides along into the 256-byte tail of its buffer (all
+  // 64 lanes load the same word), so the softmax reads it from LDS: no
+  // scalar load, whose out-of-order return would make every LDS wait a full
+  // wait.
   auto load_k = [&](int t, int8_t* buf) {
     const int8_t* src = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D;
 #pragma unroll
-    for (int piece = wave; piece < KPIECES; piece += NW)
+    for (int j = 0; j < KPW; ++j) {
+      const int piece = (wave + NW * j) % KPIECES;
       lds_dma16(src + k_src_off(piece), buf + piece * 1024);
+    }
+    lds_dma4(kscale + t, buf + G::KBUF);
+  };
+  auto tile_kscale = [&](const int8_t* buf) {
+    return *reinterpret_cast<const float*>(buf + G::KBUF);
   };
   auto load_v = [&](int t, int8_t* buf) {
     const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)t * kKT) * D);
 #pragma unroll
-    for (int piece = wave; piece < VPIECES; piece += NW)
+    for (int j = 0; j < VPW; ++j) {
+      const int piece = (wave + NW * j) % VPIECES;
       lds_dma16(src + v_src_off(piece), buf + piece * 1024);
+    }
   };
-  // loads one wave issues per K / V tile (the fewest over the waves: waiting
-  // for that many to remain outstanding is safe for every wave)
-  constexpr int KPW = KPIECES / NW;
-  auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // Waits go through the s_waitcnt builtin (not inline asm) so that the
+  // compiler's own wait insertion knows which loads have already landed and
+  // adds no full wait in front of the LDS reads. Encoding (gfx9): vmcnt in
+  // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; unused fields at maximum.
+  auto wait_all = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
   // workgroup barrier without the compiler's implied full memory wait: the
   // LDS DMA loads this wave still has in flight target buffers nobody reads
   // before the next barrier, and its own LDS reads are drained here
   auto barrier = [] {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  };
-  // wait for every load of this wave except this iteration's K loads (issued
-  // last) when there are some
-  auto wait_older = [&](bool k_pending, bool) {
-    if (k_pending && KPW > 0) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KPW) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
   };
 
   // ---- compute helpers -----------------------------------------------------------
@@ -315,18 +377,25 @@ void attn_fwd_kernel(FwdArgs a) {
   v16i magic;
 #pragma unroll
   for (int r = 0; r < 16; ++r) magic[r] = 0x4B400000;
+  const int8_t* q_wave = q_lds + (QL ? wave * 32 * D : 0);
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
+      v4i qv[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (QL) qv[qb] = *reinterpret_cast<const v4i*>(q_wave + k_frag_off[ks]);
+        else qv[qb] = qf[qb][ks];
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const v4i kf = *reinterpret_cast<const v4i*>(kbuf + kb * 32 * G::KROW + k_frag_off[ks]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (ks == 0) {
-            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], magic, 0, 0, 0);
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], magic, 0, 0, 0);
           } else {
-            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], s[kb][qb], 0, 0, 0);
           }
         }
       }
@@ -334,62 +403,49 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // softmax of one tile, one 32-query block at a time: S (kMagic-biased
-  // floats) -> P packed in the B-operand layout of the P V product
+  // floats) -> P packed in the B-operand layout of the P V product. It moves
+  // the exponent reference, rescales l and returns the accumulator's rescale
+  // factor corr (1 where the reference stayed); the caller applies corr to acc
+  // once the previous tile's P V has been accumulated. Masked keys carry the
+  // bits of -inf (see mask_tile) and get P = 0.
+  //
+  // The row max runs on the integer bits: every biased S is a positive float
+  // (kMagic + S with |S| < 2^22), so integer order is float order, and
+  // v_max3_i32 needs none of the NaN handling of the float max.
   constexpr float kMagic = 12582912.0f;
-  auto softmax = [&](const v16i (&s)[2][QB], int t, op_t (&pf)[2][QB][2]) {
-    const float alpha = alpha_q * kscale[__builtin_amdgcn_readfirstlane(t)];
-    const bool diag = CAUSAL && t * kKT + kKT - 1 > row0;
+  auto softmax = [&](const v16i (&s)[2][QB], float alpha, op_t (&pf)[2][QB][2], float (&corr)[QB],
+                     bool& any_move) {
+    any_move = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float f[32];
+      int si[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // copy the element out first: __builtin_bit_cast of a vector
-          // element reads the vector's first element
-          const int si = s[kb][qb][r];
-          f[16 * kb + r] = __builtin_bit_cast(float, si);
-        }
-      if (diag) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = t * kKT + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > row0 + 32 * qb + l32) f[16 * kb + r] = -__builtin_inff();
-          }
-      }
+        for (int r = 0; r < 16; ++r) si[16 * kb + r] = s[kb][qb][r];
       // row max: a max3 tree over the lane's 32 keys, then the other half-row
-      float m8[11];
+      int m8[11];
 #pragma unroll
-      for (int j = 0; j < 10; ++j) m8[j] = __builtin_fmaxf(__builtin_fmaxf(f[3 * j], f[3 * j + 1]), f[3 * j + 2]);
-      m8[10] = __builtin_fmaxf(f[30], f[31]);
-      const float m4a = __builtin_fmaxf(__builtin_fmaxf(m8[0], m8[1]), m8[2]);
-      const float m4b = __builtin_fmaxf(__builtin_fmaxf(m8[3], m8[4]), m8[5]);
-      const float m4c = __builtin_fmaxf(__builtin_fmaxf(m8[6], m8[7]), m8[8]);
-      const float m4d = __builtin_fmaxf(m8[9], m8[10]);
-      float mx = __builtin_fmaxf(__builtin_fmaxf(m4a, m4b), __builtin_fmaxf(m4c, m4d));
+      for (int j = 0; j < 10; ++j) m8[j] = max(max(si[3 * j], si[3 * j + 1]), si[3 * j + 2]);
+      m8[10] = max(si[30], si[31]);
+      const int m4a = max(max(m8[0], m8[1]), m8[2]);
+      const int m4b = max(max(m8[3], m8[4]), m8[5]);
+      const int m4c = max(max(m8[6], m8[7]), m8[8]);
+      const int m4d = max(m8[9], m8[10]);
+      int mxi = max(max(m4a, m4b), max(m4c, m4d));
       {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, mx),
-                                                         __builtin_bit_cast(int, mx), false, false);
-        mx = __builtin_fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+        const auto sw = __builtin_amdgcn_permlane32_swap(mxi, mxi, false, false);
+        mxi = max((int)sw[0], (int)sw[1]);
       }
-      // fl32(max S * alpha): the subtraction is exact (same binade)
-      const float mc = __builtin_fmaxf(m_ref[qb], (mx - kMagic) * alpha);
+      // fl32(max S * alpha): the subtraction is exact (same binade); a fully
+      // masked row gives -inf
+      const float mx = (__builtin_bit_cast(float, mxi) - kMagic) * alpha;
+      const float mc = __builtin_fmaxf(m_ref[qb], mx);
       const bool move = mc > m_ref[qb] + kTau;
-      if (__ballot(move) != 0) {
-        float corr = 1.0f;
-        if (move) {
-          corr = (m_ref[qb] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_ref[qb] - mc);
-          m_ref[qb] = mc;
-        }
-        l_run[qb] *= corr;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr;
-      }
+      any_move |= __ballot(move) != 0;
+      const float m_old = m_ref[qb];
+      corr[qb] = move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
+      m_ref[qb] = move ? mc : m_old;
       const float m_use = (m_ref[qb] == -__builtin_inff()) ? 0.0f : m_ref[qb];
       float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -399,7 +455,9 @@ void attn_fwd_kernel(FwdArgs a) {
           op_t pk;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float d = f[16 * kb + 8 * half + e] - kMagic;  // exact: S as a float
+            // exact: S as a float (copy the element out first: a bit-cast
+            // of a vector element reads the vector's first element)
+            const float d = __builtin_bit_cast(float, si[16 * kb + 8 * half + e]) - kMagic;
             pk[e] = (el_t)__builtin_amdgcn_exp2f(__builtin_fmaf(d, alpha, -m_use));
           }
           // four independent fp32 partial sums of the rounded P
@@ -410,7 +468,40 @@ void attn_fwd_kernel(FwdArgs a) {
           }
           pf[kb][qb][half] = pk;
         }
-      l_run[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      l_run[qb] = l_run[qb] * corr[qb] + ((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    }
+  };
+  // causal mask of tile t, in place: keys past a lane's query row get the bits
+  // of -inf. As an integer that is negative, so it loses every row max
+  // against the (positive) biased values; as a float it gives exp2 = 0.
+  auto mask_tile = [&](v16i (&s)[2][QB], int t) {
+    constexpr int kMaskedBits = (int)0xFF800000u;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // element (kb, r) holds key t*64 + 4h + off: masked when off > lim
+      const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        v16i x = s[kb][qb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const int e = x[r];
+          x[r] = off > lim ? kMaskedBits : e;
+        }
+        s[kb][qb] = x;
+      }
+    }
+  };
+  // acc *= corr, skipped by the whole wave when no row moved its reference
+  auto rescale = [&](const float (&corr)[QB], bool any_move) {
+    if (any_move) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr[qb];
     }
   };
 
@@ -426,13 +517,15 @@ void attn_fwd_kernel(FwdArgs a) {
     const int slot = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
     v_frag_off[db] = vr_lane * G::VROW + ((slot ^ G::vswz(vr_lane)) * 16) + 8 * (lane & 1);
   }
+  // channel blocks innermost: consecutive matrix instructions update
+  // different accumulators, so none waits for the one before it
   auto pv = [&](const int8_t* vbuf, const op_t (&pf)[2][QB][2]) {
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
+        for (int db = 0; db < G::DB; ++db) {
           const int8_t* p = vbuf + (kb * 32 + 16 * half) * G::VROW + v_frag_off[db];
           const v4s lo = lds_read_tr16(p);
           const v4s hi = lds_read_tr16(p + 8 * G::VROW);
@@ -444,71 +537,84 @@ void attn_fwd_kernel(FwdArgs a) {
   };
 
   // ---- pipeline ---------------------------------------------------------------------
-  if (ntiles > 0) load_v(tile_of(0), v_lds0);
-  if (ntiles > 0) load_k(tile_of(0), k_lds0);
-  if (ntiles > 1) load_k(tile_of(1), k_lds1);
-  if (ntiles > 2) load_k(tile_of(2), k_lds2);
+  // Tile j's K (with its scale) and V live in buffer j % NBUF. Iteration it
+  // issues the loads of tile it+NBUF-1 into buffer (it-1) % NBUF (its last
+  // readers ran in iteration it-1, before the previous barrier), computes
+  // S = K Q^T, the softmax and P V of tile it, then waits until only the loads
+  // of the last NBUF-2 iterations are in flight (tile it+1 has landed) and
+  // passes the barrier. Each wave runs its tile in sequence; the other waves
+  // on its SIMD fill the gaps (matrix and vector work overlap across waves).
+  // Tiles past the end are clamped to the last tile (never read), so each
+  // iteration issues the same loads. The loop is unrolled NBUF times so that
+  // every buffer is named at compile time.
+  static_for<0, NBUF - 1>([&](auto j) {
+    const int tt = tile_of(min((int)j, ntiles - 1));
+    load_k(tt, kbuf(j));
+    load_v(tt, vbuf(j));
+  });
+  if constexpr (QL) {
+    // this wave's Q fragments into its LDS slot (row l32, chunk 2ks+h,
+    // swizzled like a K block)
+    if (wave_live) {
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks)
+        *reinterpret_cast<v4i*>(q_lds + wave * 32 * D + k_frag_off[ks]) = qf[0][ks];
+    }
+  }
   wait_all();
   __syncthreads();
 
-  // Ping-pong roles (dense, 8 waves: waves w and w+4 share a SIMD). Role A
-  // runs softmax(t), P V(t), S(t+1); role B runs P V(t-1), softmax(t), S(t+1),
-  // so on each SIMD one wave's softmax (VALU) runs against the other's matrix
-  // products. B keeps P(t-1) across the barrier and finishes with P V(last).
-  constexpr bool kPingPong = !SPARSE && NW == 8;
-  const bool role_b = kPingPong && wave >= 4;
+  constexpr int kLoadsPerIt = KPW + 1 + VPW;  // K pieces, the K scale, V pieces
+  constexpr auto vmcnt = [](int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); };
+  static_assert((NBUF - 2) * kLoadsPerIt < 64, "vmcnt range");
+  constexpr std::integral_constant<bool, true> kYes{};
+  constexpr std::integral_constant<bool, false> kNo{};
 
-  v16i s[2][QB];
-  op_t p_prev[2][QB][2];
-  bool have_prev = false;
-  if (ntiles > 0 && wave_needs(tile_of(0))) qk(k_lds0, s);
-  // one tile. Buffers: tile j's K and V live in buffer j % 3. The loads of
-  // iteration it go to V(it+1) -> (it+1) % 3 (last read by role B at it-1)
-  // and K(it+3) -> it % 3 (K(it) was last read at it-1); V is issued first so
-  // that waiting for it leaves only this iteration's K loads in flight.
-  auto step = [&](int it, int8_t* k_cur, int8_t* k_next, const int8_t* v_prev,
-                  const int8_t* v_cur, int8_t* v_next) {
-    const int t = tile_of(it);
-    const bool pre_v = it + 1 < ntiles;
-    const bool pre_k = it + 3 < ntiles;
-    if (pre_v) load_v(tile_of(it + 1), v_next);
-    if (pre_k) load_k(tile_of(it + 3), k_cur);
-    const bool need = wave_needs(t);
-    if (role_b) {
-      if (have_prev) pv(v_prev, p_prev);
-      op_t pf[2][QB][2];
-      if (need) softmax(s, t, pf);
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-#pragma unroll
-        for (int y = 0; y < QB; ++y)
-#pragma unroll
-          for (int z = 0; z < 2; ++z) p_prev[x][y][z] = pf[x][y][z];
-      have_prev = need;
-    } else if (need) {
-      op_t pf[2][QB][2];
-      softmax(s, t, pf);
-      pv(v_cur, pf);
+  auto step = [&](auto jc, int it, auto masked_c) {
+    constexpr int J = decltype(jc)::value;
+    const std::integral_constant<int, J % NBUF> cur{};
+    const std::integral_constant<int, (J + NBUF - 1) % NBUF> nxt{};
+    // the next tile's loads go out once this tile's S products are queued
+    const int tl = tile_of(min(it + NBUF - 1, ntiles - 1));
+    if (wave_live) {
+      const int t = tile_of(it);
+      v16i s[2][QB];
+      qk(kbuf(cur), s);
+      load_k(tl, kbuf(nxt));
+      load_v(tl, vbuf(nxt));
+      if constexpr (decltype(masked_c)::value) mask_tile(s, t);
+      op_t p[2][QB][2];
+      float corr[QB];
+      bool any_move;
+      softmax(s, alpha_q * tile_kscale(kbuf(cur)), p, corr, any_move);
+      rescale(corr, any_move);
+      pv(vbuf(cur), p);
+    } else {
+      load_k(tl, kbuf(nxt));
+      load_v(tl, vbuf(nxt));
     }
-    if (it + 1 < ntiles && wave_needs(tile_of(it + 1))) qk(k_next, s);
-    wait_older(pre_k, false);
+    // The masked steps (a few per workgroup) wait for every load: any memory
+    // instruction the compiler adds there is then covered too.
+    if constexpr (decltype(masked_c)::value) {
+      wait_all();
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt((NBUF - 2) * kLoadsPerIt));
+    }
     barrier();
   };
-  int it = 0;
-  for (; it + 3 <= ntiles; it += 3) {
-    step(it, k_lds0, k_lds1, v_lds2, v_lds0, v_lds1);
-    step(it + 1, k_lds1, k_lds2, v_lds0, v_lds1, v_lds2);
-    step(it + 2, k_lds2, k_lds0, v_lds1, v_lds2, v_lds0);
+  for (int base = 0; base < n_plain; base += NBUF) {
+    static_for<0, NBUF>([&](auto j) {
+      if (base + (int)j < n_plain) step(j, base + (int)j, kNo);
+    });
   }
-  if (it < ntiles) step(it, k_lds0, k_lds1, v_lds2, v_lds0, v_lds1);
-  if (it + 1 < ntiles) step(it + 1, k_lds1, k_lds2, v_lds0, v_lds1, v_lds2);
-  if (have_prev) {
-    // role B: the last tile's P V; its V buffer is (ntiles - 1) % 3
-    const int lb = (ntiles - 1) % 3;
-    if (lb == 0) pv(v_lds0, p_prev);
-    else if (lb == 1) pv(v_lds1, p_prev);
-    else pv(v_lds2, p_prev);
+  // the masked tiles (the last few), one step each
+  for (int it = n_plain; it < ntiles; ++it) {
+    static_for<0, NBUF>([&](auto j) {
+      if (it % NBUF == (int)j) step(j, it, kYes);
+    });
   }
+  // no load may still be landing in LDS when the workgroup ends
+  wait_all();
 
   // ---- epilogue: O = acc / l, lse --------------------------------------------------
   if (!wave_live) return;
@@ -549,20 +655,24 @@ void attn_fwd_kernel(FwdArgs a) {
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
-  constexpr int QB = QATTN_QB;          // 32-query blocks per wave
-  constexpr int WPE = QB == 1 ? 2 : 1;  // waves per SIMD
+  constexpr int QB = QATTN_QB;  // 32-query blocks per wave
+  // dense: one workgroup of NW_DENSE waves per CU (NW_DENSE / 4 waves per
+  // SIMD); sparse: one 128-row query block per 4-wave workgroup, two
+  // workgroups per CU
   constexpr int NW_DENSE = QATTN_NW_DENSE;
+  constexpr int WPE_DENSE = NW_DENSE / 4;
   constexpr int NW_SPARSE = 128 / (32 * QB);
+  static_assert(NW_DENSE % 4 == 0, "whole waves per SIMD");
   if (sparse) {
     const dim3 grid(a.B * a.Hq * a.nqb);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, WPE>), grid,
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3>), grid,
                        dim3(NW_SPARSE * 64), 0, stream, a);
   } else {
     const int rows_wg = 32 * QB * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE>), grid,
-                       dim3(NW_DENSE * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE_DENSE, 3>),
+                       grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();
 }
