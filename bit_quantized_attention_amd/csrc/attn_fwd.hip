@@ -37,6 +37,7 @@
 // taken against the stale reference (P <= 2^kTau) and the accumulator is not
 // rescaled. The move test is wave-uniform, so the rescale is skipped for the
 // whole wave in the common case.
+#include <climits>
 #include <type_traits>
 
 #include "../../include/qattn.h"
@@ -311,13 +312,15 @@ void attn_fwd_kernel(FwdArgs a) {
   // ---- staging: direct global -> LDS, 1 KB per wave instruction -------------------
   // In piece p, lane l writes slot l % SLOTS of row p*(1024/ROW) + l / SLOTS,
   // so it fetches that row's global chunk (slot ^ swizzle(row)).
-  auto k_src_off = [&](int piece) {
+  // (unsigned 32-bit offsets from a uniform base: the loads then use the
+  // scalar-base addressing form instead of per-lane 64-bit adds)
+  auto k_src_off = [&](int piece) -> uint32_t {
     const int r = piece * (1024 / G::KROW) + lane / G::KSLOTS;
-    return r * G::KROW + (((lane % G::KSLOTS) ^ G::kswz(r)) * 16);
+    return (uint32_t)(r * G::KROW + (((lane % G::KSLOTS) ^ G::kswz(r)) * 16));
   };
-  auto v_src_off = [&](int piece) {
+  auto v_src_off = [&](int piece) -> uint32_t {
     const int r = piece * (1024 / G::VROW) + lane / G::VSLOTS;
-    return r * G::VROW + (((lane % G::VSLOTS) ^ G::vswz(r)) * 16);
+    return (uint32_t)(r * G::VROW + (((lane % G::VSLOTS) ^ G::vswz(r)) * 16));
   };
   // Every wave issues the same fixed number of 1 KB loads per tile (KPW, VPW):
   // piece (wave + NW*j) % PIECES. When a tile has fewer pieces than the group
@@ -370,13 +373,6 @@ void attn_fwd_kernel(FwdArgs a) {
   int k_frag_off[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
-  // S is accumulated on top of the integer bit pattern of kMagic = 1.5 * 2^23:
-  // the int32 result M + S read as a float is exactly kMagic + S (|S| <=
-  // 128 * 127^2 < 2^22), so the softmax gets floats without a conversion and
-  // recovers S exactly with one subtraction.
-  v16i magic;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) magic[r] = 0x4B400000;
   const int8_t* q_wave = q_lds + (QL ? wave * 32 * D : 0);
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
 #pragma unroll
@@ -393,7 +389,8 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (ks == 0) {
-            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], magic, 0, 0, 0);
+            const v16i zero = {};
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], zero, 0, 0, 0);
           } else {
             s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], s[kb][qb], 0, 0, 0);
           }
@@ -402,27 +399,30 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // softmax of one tile, one 32-query block at a time: S (kMagic-biased
-  // floats) -> P packed in the B-operand layout of the P V product. It moves
-  // the exponent reference, rescales l and returns the accumulator's rescale
-  // factor corr (1 where the reference stayed); the caller applies corr to acc
-  // once the previous tile's P V has been accumulated. Masked keys carry the
-  // bits of -inf (see mask_tile) and get P = 0.
-  //
-  // The row max runs on the integer bits: every biased S is a positive float
-  // (kMagic + S with |S| < 2^22), so integer order is float order, and
-  // v_max3_i32 needs none of the NaN handling of the float max.
-  constexpr float kMagic = 12582912.0f;
-  auto softmax = [&](const v16i (&s)[2][QB], float alpha, op_t (&pf)[2][QB][2], float (&corr)[QB],
-                     bool& any_move) {
+  // softmax of one tile, one 32-query block at a time: S (exact int32) -> P
+  // packed in the B-operand layout of the P V product. It moves the exponent
+  // reference, rescales l and returns the accumulator's rescale factor corr (1
+  // where the reference stayed; any_move says whether any row moved); the
+  // caller applies corr to acc before this tile's P V. The row max is an
+  // integer max3 tree (no NaN handling). With MASKED (causal tiles reaching
+  // past the workgroup's first row), element (kb, r), which holds key
+  // t*64 + 4h + off, is dropped when off > lim.
+  auto softmax = [&](auto masked_c, const v16i (&s)[2][QB], float alpha, int t,
+                     op_t (&pf)[2][QB][2], float (&corr)[QB], bool& any_move) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     any_move = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
       int si[32];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) si[16 * kb + r] = s[kb][qb][r];
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          const int x = s[kb][qb][r];
+          si[16 * kb + r] = (MASKED && off > lim) ? INT_MIN : x;
+        }
       // row max: a max3 tree over the lane's 32 keys, then the other half-row
       int m8[11];
 #pragma unroll
@@ -437,9 +437,9 @@ void attn_fwd_kernel(FwdArgs a) {
         const auto sw = __builtin_amdgcn_permlane32_swap(mxi, mxi, false, false);
         mxi = max((int)sw[0], (int)sw[1]);
       }
-      // fl32(max S * alpha): the subtraction is exact (same binade); a fully
-      // masked row gives -inf
-      const float mx = (__builtin_bit_cast(float, mxi) - kMagic) * alpha;
+      // fl32(max S * alpha) (S converts exactly: |S| < 2^24); in a fully
+      // masked row every P is dropped below whatever the reference is
+      const float mx = (float)mxi * alpha;
       const float mc = __builtin_fmaxf(m_ref[qb], mx);
       const bool move = mc > m_ref[qb] + kTau;
       any_move |= __ballot(move) != 0;
@@ -455,10 +455,11 @@ void attn_fwd_kernel(FwdArgs a) {
           op_t pk;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            // exact: S as a float (copy the element out first: a bit-cast
-            // of a vector element reads the vector's first element)
-            const float d = __builtin_bit_cast(float, si[16 * kb + 8 * half + e]) - kMagic;
-            pk[e] = (el_t)__builtin_amdgcn_exp2f(__builtin_fmaf(d, alpha, -m_use));
+            const int i = 16 * kb + 8 * half + e;
+            const int off = kb * 32 + 8 * ((8 * half + e) >> 2) + (e & 3);
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[i], alpha, -m_use));
+            if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
+            pk[e] = (el_t)pe;
           }
           // four independent fp32 partial sums of the rounded P
 #pragma unroll
@@ -469,28 +470,6 @@ void attn_fwd_kernel(FwdArgs a) {
           pf[kb][qb][half] = pk;
         }
       l_run[qb] = l_run[qb] * corr[qb] + ((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-    }
-  };
-  // causal mask of tile t, in place: keys past a lane's query row get the bits
-  // of -inf. As an integer that is negative, so it loses every row max
-  // against the (positive) biased values; as a float it gives exp2 = 0.
-  auto mask_tile = [&](v16i (&s)[2][QB], int t) {
-    constexpr int kMaskedBits = (int)0xFF800000u;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // element (kb, r) holds key t*64 + 4h + off: masked when off > lim
-      const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        v16i x = s[kb][qb];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          const int e = x[r];
-          x[r] = off > lim ? kMaskedBits : e;
-        }
-        s[kb][qb] = x;
-      }
     }
   };
   // acc *= corr, skipped by the whole wave when no row moved its reference
@@ -582,11 +561,10 @@ void attn_fwd_kernel(FwdArgs a) {
       qk(kbuf(cur), s);
       load_k(tl, kbuf(nxt));
       load_v(tl, vbuf(nxt));
-      if constexpr (decltype(masked_c)::value) mask_tile(s, t);
       op_t p[2][QB][2];
       float corr[QB];
       bool any_move;
-      softmax(s, alpha_q * tile_kscale(kbuf(cur)), p, corr, any_move);
+      softmax(masked_c, s, alpha_q * tile_kscale(kbuf(cur)), t, p, corr, any_move);
       rescale(corr, any_move);
       pv(vbuf(cur), p);
     } else {
