@@ -48,6 +48,13 @@ int32_t max_keep_of(const Shape& s, int32_t num, int32_t den) {
 
 qattn_status_t launched(hipError_t e) { return e == hipSuccess ? QATTN_OK : QATTN_ERR_DEVICE; }
 
+// Both preprocessing calls share one workspace of this size.
+size_t workspace_of(const Shape& s) {
+  const size_t a = qattn::ksum_workspace_bytes(s);
+  const size_t b = qattn::mask_workspace_bytes(s);
+  return a > b ? a : b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -71,9 +78,7 @@ const char* qattn_version(void) { return "qattn 0.1.0 gfx950"; }
 size_t qattn_workspace_bytes(const qattn_problem_t* p) {
   Shape s;
   if (check_problem(p, &s) != QATTN_OK) return 0;
-  const size_t a = qattn::ksum_workspace_bytes(s);
-  const size_t b = qattn::mask_workspace_bytes(s);
-  return a > b ? a : b;
+  return workspace_of(s);
 }
 
 int32_t qattn_max_keep(const qattn_problem_t* p, int32_t keep_num, int32_t keep_den) {
@@ -94,7 +99,7 @@ qattn_status_t qattn_smooth_quant(const qattn_problem_t* p, const void* q, const
   const void* ptrs[] = {q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool, workspace};
   for (const void* x : ptrs)
     if (x && misaligned(x)) return QATTN_ERR_ALIGN;
-  if (workspace_bytes < qattn::ksum_workspace_bytes(s)) return QATTN_ERR_ARG;
+  if (workspace_bytes < workspace_of(s)) return QATTN_ERR_ARG;
   return launched(qattn::launch_smooth_quant(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool,
                                              k_pool, workspace,
                                              static_cast<hipStream_t>(stream)));
@@ -114,7 +119,7 @@ qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool, c
     if (misaligned(x)) return QATTN_ERR_ALIGN;
   if (!ratio_ok(keep_num, keep_den)) return QATTN_ERR_ARG;
   if (max_keep < max_keep_of(s, keep_num, keep_den)) return QATTN_ERR_ARG;
-  if (workspace_bytes < qattn::mask_workspace_bytes(s)) return QATTN_ERR_ARG;
+  if (workspace_bytes < workspace_of(s)) return QATTN_ERR_ARG;
   return launched(qattn::launch_block_mask(s, q_pool, k_pool, keep_num, keep_den, max_keep, kv_idx,
                                            kv_cnt, workspace, static_cast<hipStream_t>(stream)));
 }

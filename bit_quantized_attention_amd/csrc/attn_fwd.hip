@@ -59,6 +59,14 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;             // keys per tile
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
+// The INT8 product accumulates onto the bit pattern of 1.5 * 2^23: every
+// |S| < 2^22 (d * 127^2 at most) then reads, as an fp32 number, exactly
+// 1.5 * 2^23 + S, so no conversion instruction is needed.
+constexpr int kSBias = 0x4B400000;
+constexpr float kSBiasF = 12582912.0f;
+// A lane's partial row sum above this (2^(kTau-1)) may hide an element past
+// the reference by more than kTau; only then is the row max computed.
+constexpr float kSumFilter = 128.0f;
 constexpr int kMaxSparseTiles = 2048;
 
 template <bool BF16>
@@ -164,33 +172,28 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int RW = 32 * QB;
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
-  // NBUF K and NBUF V buffers as distinct objects, always named with
-  // compile-time indices: the compiler can then tell that an LDS read of one
-  // buffer does not depend on the DMA loads still landing in another, and
-  // waits only for the loads of the buffer it reads
+  // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
+  // LDS object, always named with a compile-time index: the compiler can then
+  // tell that an LDS read of one buffer does not depend on the DMA loads still
+  // landing in another, and waits only for the loads of the buffer it reads.
+  // (Its tracking has room for few objects; one per stage keeps every read of
+  // the loop clear of the loads in flight.)
   static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
-  __shared__ __attribute__((aligned(16))) int8_t k_lds0[G::KBUF + 256];
-  __shared__ __attribute__((aligned(16))) int8_t k_lds1[G::KBUF + 256];
-  __shared__ __attribute__((aligned(16))) int8_t k_lds2[G::KBUF + 256];
-  __shared__ __attribute__((aligned(16))) int8_t k_lds3[NBUF == 4 ? G::KBUF + 256 : 16];
-  __shared__ __attribute__((aligned(16))) int8_t v_lds0[G::VBUF];
-  __shared__ __attribute__((aligned(16))) int8_t v_lds1[G::VBUF];
-  __shared__ __attribute__((aligned(16))) int8_t v_lds2[G::VBUF];
-  __shared__ __attribute__((aligned(16))) int8_t v_lds3[NBUF == 4 ? G::VBUF : 16];
-  auto kbuf = [&](auto i) -> int8_t* {
+  constexpr int KB = G::KBUF + 256;  // K tile plus the tail carrying its scale
+  constexpr int SB = KB + G::VBUF;   // one stage
+  __shared__ __attribute__((aligned(16))) int8_t stage0[SB];
+  __shared__ __attribute__((aligned(16))) int8_t stage1[SB];
+  __shared__ __attribute__((aligned(16))) int8_t stage2[SB];
+  __shared__ __attribute__((aligned(16))) int8_t stage3[NBUF == 4 ? SB : 16];
+  auto stage = [&](auto i) -> int8_t* {
     constexpr int j = decltype(i)::value % NBUF;
-    if constexpr (j == 0) return k_lds0;
-    else if constexpr (j == 1) return k_lds1;
-    else if constexpr (j == 2) return k_lds2;
-    else return k_lds3;
+    if constexpr (j == 0) return stage0;
+    else if constexpr (j == 1) return stage1;
+    else if constexpr (j == 2) return stage2;
+    else return stage3;
   };
-  auto vbuf = [&](auto i) -> int8_t* {
-    constexpr int j = decltype(i)::value % NBUF;
-    if constexpr (j == 0) return v_lds0;
-    else if constexpr (j == 1) return v_lds1;
-    else if constexpr (j == 2) return v_lds2;
-    else return v_lds3;
-  };
+  auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
+  auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
   // Dense workgroups keep each wave's Q fragments in LDS (same swizzle as a
   // K block) and read them per tile: that frees the 16 registers they would
   // hold for the whole kernel. Sparse workgroups keep them in registers (their
@@ -374,6 +377,15 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
   const int8_t* q_wave = q_lds + (QL ? wave * 32 * D : 0);
+  // (held in registers for the whole loop: the empty asm hides the constant,
+  // so it is not rematerialized with 16 moves per tile)
+  v16i sbias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    int bv = kSBias;
+    asm volatile("" : "+v"(bv));
+    sbias[r] = bv;
+  }
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
@@ -389,8 +401,7 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           if (ks == 0) {
-            const v16i zero = {};
-            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], zero, 0, 0, 0);
+            s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], sbias, 0, 0, 0);
           } else {
             s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qv[qb], s[kb][qb], 0, 0, 0);
           }
@@ -399,88 +410,104 @@ void attn_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // softmax of one tile, one 32-query block at a time: S (exact int32) -> P
-  // packed in the B-operand layout of the P V product. It moves the exponent
-  // reference, rescales l and returns the accumulator's rescale factor corr (1
-  // where the reference stayed; any_move says whether any row moved); the
-  // caller applies corr to acc before this tile's P V. The row max is an
-  // integer max3 tree (no NaN handling). With MASKED (causal tiles reaching
-  // past the workgroup's first row), element (kb, r), which holds key
-  // t*64 + 4h + off, is dropped when off > lim.
+  // softmax of one tile, one 32-query block at a time: S (as 1.5*2^23 + S in
+  // fp32) -> P packed in the B-operand layout of the P V product, the lane's
+  // partial row sum (fp32, of P before its 16-bit rounding) added to l.
+  // With A = alpha * 1.5*2^23 split into A_hi + A_lo (exact), the fma
+  // alpha*Sb - A_hi is alpha*S + A_lo, so the exponent alpha*S - m is
+  // fma(alpha, Sb, -A_hi) - (m + A_lo): two roundings of numbers of the size
+  // of the exponent itself.
+  // The reference m follows the rule of the module comment, but the row max
+  // is only formed when some lane's partial sum exceeds kSumFilter: a move
+  // needs an element more than kTau above m, i.e. a P above 2^kTau. Then the
+  // row max (an integer max3 tree) decides; rows that move get P again
+  // against the new reference, and acc and l are rescaled (corr). With
+  // MASKED (causal tiles reaching past the workgroup's first row), element
+  // (kb, r), which holds key t*64 + 4h + off, is dropped when off > lim.
+  // hook(g) runs at the start of group g = 2*kb + half of the first pass
+  // (the lagged P V products of the previous tile interleave there).
   auto softmax = [&](auto masked_c, const v16i (&s)[2][QB], float alpha, int t,
-                     op_t (&pf)[2][QB][2], float (&corr)[QB], bool& any_move) {
+                     op_t (&pf)[2][QB][2], auto&& hook) {
     constexpr bool MASKED = decltype(masked_c)::value;
-    any_move = false;
+    const float a_hi = alpha * kSBiasF;
+    const float a_lo = __builtin_fmaf(alpha, kSBiasF, -a_hi);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
-      int si[32];
+      // P against reference m (-inf: every visible P is +inf, which forces
+      // the row max below), and its partial sum
+      auto exps = [&](float m, float ahi, auto&& grp_hook) -> float {
+        const float cm = m + a_lo;
+        float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        static_for<0, 4>([&](auto gc) {
+          constexpr int kb = decltype(gc)::value >> 1;
+          constexpr int half = decltype(gc)::value & 1;
+          grp_hook(gc);
+          {
+            op_t pk;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * half + e;
+              const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+              const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
+              const float x = __builtin_fmaf(alpha, sb, -ahi) - cm;
+              float pe = __builtin_amdgcn_exp2f(x);
+              if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
+              lsum[e & 3] += pe;
+              pk[e] = (el_t)pe;
+            }
+            pf[kb][qb][half] = pk;
+          }
+        });
+        return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      };
+      float psum = exps(m_ref[qb], a_hi, hook);
+      if (__ballot(psum > kSumFilter) != 0) {
+        // row max over the lane's 32 keys (biased integers; masked keys
+        // excluded), then over the other half-row
+        int si[32];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          const int x = s[kb][qb][r];
-          si[16 * kb + r] = (MASKED && off > lim) ? INT_MIN : x;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            si[16 * kb + r] = (MASKED && off > lim) ? INT_MIN : (int)s[kb][qb][r];
+          }
+        int m8[11];
+#pragma unroll
+        for (int j = 0; j < 10; ++j) m8[j] = max(max(si[3 * j], si[3 * j + 1]), si[3 * j + 2]);
+        m8[10] = max(si[30], si[31]);
+        const int m4a = max(max(m8[0], m8[1]), m8[2]);
+        const int m4b = max(max(m8[3], m8[4]), m8[5]);
+        const int m4c = max(max(m8[6], m8[7]), m8[8]);
+        const int m4d = max(m8[9], m8[10]);
+        int mxi = max(max(m4a, m4b), max(m4c, m4d));
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(mxi, mxi, false, false);
+          mxi = max((int)sw[0], (int)sw[1]);
         }
-      // row max: a max3 tree over the lane's 32 keys, then the other half-row
-      int m8[11];
+        // fl32(max S * alpha); -inf for a fully masked row, which never moves
+        const float mx = mxi == INT_MIN ? -__builtin_inff() : (float)(mxi - kSBias) * alpha;
+        const float m_old = m_ref[qb];
+        const float mc = __builtin_fmaxf(m_old, mx);
+        const bool move = mc > m_old + kTau;
+        if (__ballot(move) != 0) {
+          const float corr =
+              move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
+          m_ref[qb] = move ? mc : m_old;
+          // recompute from S (an opaque copy of a_hi keeps the compiler from
+          // holding the 32 first-pass products live across the fast path)
+          float ahi = a_hi;
+          asm volatile("" : "+v"(ahi));
+          psum = exps(m_ref[qb], ahi, [](auto) {});
+          l_run[qb] *= corr;
 #pragma unroll
-      for (int j = 0; j < 10; ++j) m8[j] = max(max(si[3 * j], si[3 * j + 1]), si[3 * j + 2]);
-      m8[10] = max(si[30], si[31]);
-      const int m4a = max(max(m8[0], m8[1]), m8[2]);
-      const int m4b = max(max(m8[3], m8[4]), m8[5]);
-      const int m4c = max(max(m8[6], m8[7]), m8[8]);
-      const int m4d = max(m8[9], m8[10]);
-      int mxi = max(max(m4a, m4b), max(m4c, m4d));
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(mxi, mxi, false, false);
-        mxi = max((int)sw[0], (int)sw[1]);
+          for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr;
+        }
       }
-      // fl32(max S * alpha) (S converts exactly: |S| < 2^24); in a fully
-      // masked row every P is dropped below whatever the reference is
-      const float mx = (float)mxi * alpha;
-      const float mc = __builtin_fmaxf(m_ref[qb], mx);
-      const bool move = mc > m_ref[qb] + kTau;
-      any_move |= __ballot(move) != 0;
-      const float m_old = m_ref[qb];
-      corr[qb] = move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
-      m_ref[qb] = move ? mc : m_old;
-      const float m_use = (m_ref[qb] == -__builtin_inff()) ? 0.0f : m_ref[qb];
-      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          op_t pk;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 16 * kb + 8 * half + e;
-            const int off = kb * 32 + 8 * ((8 * half + e) >> 2) + (e & 3);
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf((float)si[i], alpha, -m_use));
-            if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
-            pk[e] = (el_t)pe;
-          }
-          // four independent fp32 partial sums of the rounded P
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const pair_t pr = {pk[2 * w], pk[2 * w + 1]};
-            lsum[w] = MM::sum2(pr, lsum[w]);
-          }
-          pf[kb][qb][half] = pk;
-        }
-      l_run[qb] = l_run[qb] * corr[qb] + ((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-    }
-  };
-  // acc *= corr, skipped by the whole wave when no row moved its reference
-  auto rescale = [&](const float (&corr)[QB], bool any_move) {
-    if (any_move) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][qb][r] *= corr[qb];
+      l_run[qb] += psum;
     }
   };
 
@@ -496,41 +523,74 @@ void attn_fwd_kernel(FwdArgs a) {
     const int slot = 4 * db + 2 * (grp & 1) + ((lane & 3) >> 1);
     v_frag_off[db] = vr_lane * G::VROW + ((slot ^ G::vswz(vr_lane)) * 16) + 8 * (lane & 1);
   }
-  // channel blocks innermost: consecutive matrix instructions update
-  // different accumulators, so none waits for the one before it
+  // The V^T fragments of one 16-key group g = 2*kb + half (one per channel
+  // block db)
+  auto load_vgrp = [&](const int8_t* vbuf, int g, op_t (&vf)[G::DB]) {
+    const int kb = g >> 1, half = g & 1;
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) {
+      const int8_t* p = vbuf + (kb * 32 + 16 * half) * G::VROW + v_frag_off[db];
+      const v4s lo = lds_read_tr16(p);
+      const v4s hi = lds_read_tr16(p + 8 * G::VROW);
+      const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      vf[db] = __builtin_bit_cast(op_t, both);
+    }
+  };
+  // P V over the tile's four 16-key groups, the fragments of the group after
+  // next in flight while a group's products run (two fragment sets; the
+  // scheduling barriers keep the compiler from sinking the reads next to
+  // their use, which would expose the LDS latency at every product). Channel
+  // blocks innermost: consecutive matrix instructions update different
+  // accumulators, so none waits for the one before it.
   auto pv = [&](const int8_t* vbuf, const op_t (&pf)[2][QB][2]) {
+    op_t va[G::DB], vb[G::DB];
+    load_vgrp(vbuf, 0, va);
+    load_vgrp(vbuf, 1, vb);
+    static_for<0, 4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      op_t (&vf)[G::DB] = (g & 1) ? vb : va;
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db) {
-          const int8_t* p = vbuf + (kb * 32 + 16 * half) * G::VROW + v_frag_off[db];
-          const v4s lo = lds_read_tr16(p);
-          const v4s hi = lds_read_tr16(p + 8 * G::VROW);
-          const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const op_t vf = __builtin_bit_cast(op_t, both);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[db][qb] = MM::mma(vf, pf[kb][qb][half], acc[db][qb]);
-        }
+        for (int qb = 0; qb < QB; ++qb)
+          acc[db][qb] = MM::mma(vf[db], pf[g >> 1][qb][g & 1], acc[db][qb]);
+      if constexpr (g + 2 < 4) load_vgrp(vbuf, g + 2, vf);
+    });
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- pipeline ---------------------------------------------------------------------
   // Tile j's K (with its scale) and V live in buffer j % NBUF. Iteration it
-  // issues the loads of tile it+NBUF-1 into buffer (it-1) % NBUF (its last
-  // readers ran in iteration it-1, before the previous barrier), computes
-  // S = K Q^T, the softmax and P V of tile it, then waits until only the loads
-  // of the last NBUF-2 iterations are in flight (tile it+1 has landed) and
-  // passes the barrier. Each wave runs its tile in sequence; the other waves
-  // on its SIMD fill the gaps (matrix and vector work overlap across waves).
+  // issues the loads of tile it+PD into buffer (it+PD) % NBUF, whose last
+  // readers ran before the previous barrier, computes S = K Q^T and the
+  // softmax of tile it, then waits until only the loads of the last PD-1
+  // iterations are in flight (tile it+1 has landed) and passes the barrier.
   // Tiles past the end are clamped to the last tile (never read), so each
-  // iteration issues the same loads. The loop is unrolled NBUF times so that
-  // every buffer is named at compile time.
-  static_for<0, NBUF - 1>([&](auto j) {
+  // iteration issues the same loads. The loops are unrolled NBUF times so
+  // that every buffer is named at compile time.
+  //
+  // Lagged P V (dense 8-wave workgroups): iteration it runs the P V products
+  // of tile it-1 inside the softmax of tile it, four matrix instructions per
+  // 16-key group of exponentials, so each wave keeps its matrix unit busy
+  // while its vector unit works (P of consecutive tiles alternates between
+  // two register sets; the first iteration multiplies a copy of tile 0's V
+  // by a zero P). V(it-1) is still read in iteration it, so the prefetch distance is
+  // NBUF-2. Otherwise (sparse) each wave runs S, the softmax and P V of a
+  // tile in sequence and the waves sharing a SIMD overlap each other's work.
+  constexpr bool kLAG = !SPARSE && NW == 8;
+  static_assert(!kLAG || NBUF == 4, "the lagged products keep four staging buffers");
+  constexpr int PD = kLAG ? NBUF - 2 : NBUF - 1;  // prefetch distance (tiles)
+  static_for<0, PD>([&](auto j) {
     const int tt = tile_of(min((int)j, ntiles - 1));
     load_k(tt, kbuf(j));
     load_v(tt, vbuf(j));
   });
+  // lagged: the first iteration's "previous" V buffer gets tile 0's V too, so
+  // that its zero P meets finite values (and the buffer is named at compile
+  // time: a runtime choice of LDS buffer makes the compiler wait for every
+  // load in flight before reading it)
+  if constexpr (kLAG) load_v(tile_of(0), vbuf(std::integral_constant<int, NBUF - 1>{}));
   if constexpr (QL) {
     // this wave's Q fragments into its LDS slot (row l32, chunk 2ks+h,
     // swizzled like a K block)
@@ -545,38 +605,77 @@ void attn_fwd_kernel(FwdArgs a) {
 
   constexpr int kLoadsPerIt = KPW + 1 + VPW;  // K pieces, the K scale, V pieces
   constexpr auto vmcnt = [](int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); };
-  static_assert((NBUF - 2) * kLoadsPerIt < 64, "vmcnt range");
+  static_assert((PD - 1) * kLoadsPerIt < 64, "vmcnt range");
   constexpr std::integral_constant<bool, true> kYes{};
   constexpr std::integral_constant<bool, false> kNo{};
 
+  op_t p_even[2][QB][2], p_odd[2][QB][2];  // lagged: P of even / odd tiles
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p_odd[kb][qb][hf][e] = (el_t)0.0f;
   auto step = [&](auto jc, int it, auto masked_c) {
     constexpr int J = decltype(jc)::value;
     const std::integral_constant<int, J % NBUF> cur{};
-    const std::integral_constant<int, (J + NBUF - 1) % NBUF> nxt{};
-    // the next tile's loads go out once this tile's S products are queued
-    const int tl = tile_of(min(it + NBUF - 1, ntiles - 1));
-    if (wave_live) {
-      const int t = tile_of(it);
-      v16i s[2][QB];
-      qk(kbuf(cur), s);
+    const std::integral_constant<int, (J + PD) % NBUF> nxt{};
+    const std::integral_constant<int, (J + NBUF - 1) % NBUF> prv{};
+    const int tl = tile_of(min(it + PD, ntiles - 1));
+    // Every wave issues the loads at the same place, live or not, after the
+    // reads of the current K tile: a separate branch for waves without rows
+    // would merge its freshly issued loads into the live path's wait state.
+    const int t = tile_of(it);
+    v16i s[2][QB];
+    float alpha = 0.0f;
+    if constexpr (kLAG) {
+      // (NBUF is even, so J and it have the same parity)
+      const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
+      op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
+      const int8_t* vp = vbuf(prv);
+      op_t va[G::DB], vb[G::DB];
+      if (wave_live) {
+        alpha = alpha_q * tile_kscale(kbuf(cur));
+        load_vgrp(vp, 0, va);
+        load_vgrp(vp, 1, vb);
+        qk(kbuf(cur), s);
+      }
       load_k(tl, kbuf(nxt));
       load_v(tl, vbuf(nxt));
-      op_t p[2][QB][2];
-      float corr[QB];
-      bool any_move;
-      softmax(masked_c, s, alpha_q * tile_kscale(kbuf(cur)), t, p, corr, any_move);
-      rescale(corr, any_move);
-      pv(vbuf(cur), p);
+      if (wave_live) {
+        auto lagged_pv = [&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          op_t (&vf)[G::DB] = (g & 1) ? vb : va;
+#pragma unroll
+          for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              acc[db][qb] = MM::mma(vf[db], p_in[g >> 1][qb][g & 1], acc[db][qb]);
+          if constexpr (g + 2 < 4) load_vgrp(vp, g + 2, vf);
+        };
+        softmax(masked_c, s, alpha, t, p_out, lagged_pv);
+      }
     } else {
+      if (wave_live) {
+        alpha = alpha_q * tile_kscale(kbuf(cur));
+        qk(kbuf(cur), s);
+      }
       load_k(tl, kbuf(nxt));
       load_v(tl, vbuf(nxt));
+      if (wave_live) {
+        op_t p[2][QB][2];
+        softmax(masked_c, s, alpha, t, p, [](auto) {});
+        pv(vbuf(cur), p);
+      }
     }
     // The masked steps (a few per workgroup) wait for every load: any memory
     // instruction the compiler adds there is then covered too.
     if constexpr (decltype(masked_c)::value) {
       wait_all();
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt((NBUF - 2) * kLoadsPerIt));
+      __builtin_amdgcn_s_waitcnt(vmcnt((PD - 1) * kLoadsPerIt));
     }
     barrier();
   };
@@ -593,6 +692,14 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   // no load may still be landing in LDS when the workgroup ends
   wait_all();
+  if constexpr (kLAG) {
+    // the last tile's P V (its buffer has landed and is not reloaded)
+    if (wave_live && ntiles > 0) {
+      static_for<0, NBUF>([&](auto j) {
+        if ((ntiles - 1) % NBUF == (int)j) pv(vbuf(j), (j & 1) ? p_odd : p_even);
+      });
+    }
+  }
 
   // ---- epilogue: O = acc / l, lse --------------------------------------------------
   if (!wave_live) return;
@@ -649,7 +756,8 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
     const int rows_wg = 32 * QB * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE_DENSE, 3>),
+    constexpr int NBUF_DENSE = NW_DENSE == 8 ? 4 : 3;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE_DENSE, NBUF_DENSE>),
                        grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();

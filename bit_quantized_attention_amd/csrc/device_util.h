@@ -42,26 +42,20 @@ __device__ __forceinline__ float quant_scale(float amax) {
   return s == 0.0f ? 1.0f : s;
 }
 
-// clamp(round-half-even(x / scale), -127, 127) of the exact real quotient.
-// `inv` is any approximation of 1/scale: rint(x * inv) is within one of the
-// answer, and the two fused multiply-adds decide the exact side of the
-// neighbouring half-integers (the sign of an fma result is exact).
+// clamp(round-half-even(x / scale), -127, 127) of the exact real quotient,
+// without branches. `inv` is any close approximation of 1/scale, so the true
+// quotient lies within half a unit of t = x * inv and its rounding is
+// floor(t) or floor(t) + 1. The half-integer h = floor(t) + 1/2 between the two
+// is compared with the quotient through the sign of one fused multiply-add,
+// x - h * scale (exact, because the product inside an fma is not rounded):
+// positive picks h + 1/2, negative h - 1/2, zero is a tie and rounding h itself
+// to even picks the even neighbour.
 __device__ __forceinline__ int quant_code(float x, float scale, float inv) {
-  float c = __builtin_rintf(x * inv);
-  const float up = __builtin_fmaf(-(c + 0.5f), scale, x);   // x - (c + 1/2) scale
-  const float dn = __builtin_fmaf(-(c - 0.5f), scale, x);   // x - (c - 1/2) scale
-  const int ci = (int)c;
-  if (up > 0.0f) {
-    c += 1.0f;
-  } else if (up == 0.0f) {
-    if (ci & 1) c += 1.0f;                                  // tie: the even one
-  } else if (dn < 0.0f) {
-    c -= 1.0f;
-  } else if (dn == 0.0f) {
-    if (ci & 1) c -= 1.0f;
-  }
-  c = __builtin_fminf(__builtin_fmaxf(c, -127.0f), 127.0f);
-  return (int)c;
+  const float h = __builtin_floorf(x * inv) + 0.5f;
+  const float e = __builtin_fmaf(-h, scale, x);
+  const float g = e == 0.0f ? 0.0f : __builtin_copysignf(0.5f, e);
+  float v = __builtin_fminf(__builtin_fmaxf(h + g, -127.0f), 127.0f);
+  return (int)__builtin_rintf(v);
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {

@@ -9,7 +9,7 @@ namespace qattn {
 
 constexpr int kQBlock = 128;     // query tokens per quantization block
 constexpr int kKBlock = 64;      // key tokens per quantization block
-constexpr int kKsumChunk = 512;  // tokens per partial K sum
+constexpr int kKsumChunk = 128;  // tokens per partial K sum
 
 struct Shape {
   int B, Hq, Hkv, N, d;

@@ -1,12 +1,13 @@
 // K smoothing and per-block INT8 quantization of Q and K (bandwidth-bound).
 //
 // Three launches on the caller's stream:
-//   1. ksum_partial   -- exact per-channel sums of K over 512-token chunks
-//                        (fp64 double-double), one workgroup per (chunk, b*hk);
+//   1. ksum_qquant    -- exact per-channel sums of K over 128-token chunks
+//                        (fp64 double-double), one workgroup per (chunk, b*hk),
+//                        then one workgroup per Q block (128 tokens): amax,
+//                        scale, exact RNE codes, optional pooled block means;
 //   2. kmean_finalize -- merge the chunks, k_mean = fl32(fl64(sum) / N);
-//   3. quant          -- one workgroup per Q block (128 tokens) or K block
-//                        (64 tokens): amax, scale, exact RNE codes, optional
-//                        pooled block means.
+//   3. kquant         -- one workgroup per K block (64 tokens), smoothed by
+//                        k_mean, as for Q.
 // Every element is read with 16-byte vector loads; a 64-lane wave covers 4
 // (d = 128) or 8 (d = 64) contiguous rows per load instruction.
 #include "device_util.h"
@@ -21,15 +22,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Exact per-channel sums of K over one chunk of kKsumChunk tokens of head bh.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void ksum_partial_kernel(const uint16_t* __restrict__ k,
-                                                                double2* __restrict__ part,
-                                                                int N, int nchunk) {
+__device__ __forceinline__ void ksum_chunk(const uint16_t* __restrict__ k,
+                                           double2* __restrict__ part, int N, int nchunk,
+                                           int chunk, int bh, double2 (*red)[D]) {
   constexpr int LPR = D / 8;          // lanes per row (16 bytes each)
   constexpr int RPI = kThreads / LPR; // rows per iteration
-  __shared__ double2 red[RPI][D];
-  const int chunk = blockIdx.x;
-  const int bh = blockIdx.y;
   const int cg = threadIdx.x % LPR;
   const int rg = threadIdx.x / LPR;
   const int t0 = chunk * kKsumChunk;
@@ -55,18 +54,47 @@ __global__ __launch_bounds__(kThreads) void ksum_partial_kernel(const uint16_t* 
   }
 }
 
-__global__ __launch_bounds__(128) void kmean_finalize_kernel(const double2* __restrict__ part,
-                                                             float* __restrict__ k_mean,
-                                                             int N, int nchunk, int D) {
+// One workgroup of kFinGroups x kFinChans threads per (b, hk, slice of
+// kFinChans channels): group g merges chunks g, g + kFinGroups, ... of its
+// channel (four loads in flight), then the groups merge pairwise in LDS. The
+// double-double sums are exact for any realistic K, so the order is free.
+constexpr int kFinGroups = 32;
+constexpr int kFinChans = 32;
+
+__global__ __launch_bounds__(kFinGroups * kFinChans) void kmean_finalize_kernel(
+    const double2* __restrict__ part, float* __restrict__ k_mean, int N, int nchunk, int D) {
+  __shared__ double2 red[kFinGroups][kFinChans];
   const int bh = blockIdx.x;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    double H = 0.0, L = 0.0;
-    for (int ch = 0; ch < nchunk; ++ch) {
-      const double2 v = part[((size_t)bh * nchunk + ch) * D + c];
-      dd_merge(H, L, v.x, v.y);
+  const int cs = threadIdx.x % kFinChans;
+  const int g = threadIdx.x / kFinChans;
+  const int c = blockIdx.y * kFinChans + cs;
+  const double2* src = part + (size_t)bh * nchunk * D + c;
+  double H = 0.0, L = 0.0;
+  int ch = g;
+  for (; ch + 3 * kFinGroups < nchunk; ch += 4 * kFinGroups) {
+    double2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[(size_t)(ch + u * kFinGroups) * D];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dd_merge(H, L, v[u].x, v[u].y);
+  }
+  for (; ch < nchunk; ch += kFinGroups) {
+    const double2 v = src[(size_t)ch * D];
+    dd_merge(H, L, v.x, v.y);
+  }
+  red[g][cs] = make_double2(H, L);
+#pragma unroll
+  for (int w = kFinGroups / 2; w >= 1; w /= 2) {
+    __syncthreads();
+    if (g < w) {
+      const double2 o = red[g + w][cs];
+      dd_merge(H, L, o.x, o.y);
+      red[g][cs] = make_double2(H, L);
     }
-    const double s = H + L;  // the fp64 value nearest the exact sum
-    k_mean[(size_t)bh * D + c] = (float)(s / (double)N);
+  }
+  if (g == 0) {
+    const double sum = H + L;  // the fp64 value nearest the exact sum
+    k_mean[(size_t)bh * D + c] = (float)(sum / (double)N);
   }
 }
 
@@ -160,30 +188,43 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ src,
   }
 }
 
+// Pass 1: the K chunk sums (first, so that the finalize can start early) and
+// every Q block, which does not depend on the K mean.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
+__global__ __launch_bounds__(kThreads) void ksum_qquant_kernel(QuantArgs a, double2* part,
+                                                               int nchunk, int nsum) {
   constexpr int RPI = kThreads / (D / 8);
   __shared__ double2 red[RPI][D];
   __shared__ float wmax[kThreads / 64];
   const int blk = blockIdx.x;
-  if (blk < a.nQ) {
-    const size_t bh = blk / a.nqb;  // b * Hq + hq
-    const int i = blk % a.nqb;
-    const size_t row0 = bh * a.N + (size_t)i * kQBlock;
-    quant_block<D, BF16, kQBlock, false>(a.q + row0 * D, nullptr, a.q_i8 + row0 * D,
-                                         a.q_scale + blk,
-                                         a.q_pool ? a.q_pool + (size_t)blk * D : nullptr, red,
-                                         wmax);
-  } else {
-    const int kblk = blk - a.nQ;
-    const size_t bh = kblk / a.nkb;  // b * Hkv + hk
-    const int j = kblk % a.nkb;
-    const size_t row0 = bh * a.N + (size_t)j * kKBlock;
-    quant_block<D, BF16, kKBlock, true>(a.k + row0 * D, a.k_mean + bh * D, a.k_i8 + row0 * D,
-                                        a.k_scale + kblk,
-                                        a.k_pool ? a.k_pool + (size_t)kblk * D : nullptr, red,
-                                        wmax);
+  if (blk < nsum) {
+    ksum_chunk<D, BF16>(a.k, part, a.N, nchunk, blk % nchunk, blk / nchunk, red);
+    return;
   }
+  const int qblk = blk - nsum;
+  const size_t bh = qblk / a.nqb;  // b * Hq + hq
+  const int i = qblk % a.nqb;
+  const size_t row0 = bh * a.N + (size_t)i * kQBlock;
+  quant_block<D, BF16, kQBlock, false>(a.q + row0 * D, nullptr, a.q_i8 + row0 * D,
+                                       a.q_scale + qblk,
+                                       a.q_pool ? a.q_pool + (size_t)qblk * D : nullptr, red,
+                                       wmax);
+}
+
+// Pass 3: every K block, smoothed by the finished K mean.
+template <int D, bool BF16>
+__global__ __launch_bounds__(kThreads) void kquant_kernel(QuantArgs a) {
+  constexpr int RPI = kThreads / (D / 8);
+  __shared__ double2 red[RPI][D];
+  __shared__ float wmax[kThreads / 64];
+  const int kblk = blockIdx.x;
+  const size_t bh = kblk / a.nkb;  // b * Hkv + hk
+  const int j = kblk % a.nkb;
+  const size_t row0 = bh * a.N + (size_t)j * kKBlock;
+  quant_block<D, BF16, kKBlock, true>(a.k + row0 * D, a.k_mean + bh * D, a.k_i8 + row0 * D,
+                                      a.k_scale + kblk,
+                                      a.k_pool ? a.k_pool + (size_t)kblk * D : nullptr, red,
+                                      wmax);
 }
 
 template <int D, bool BF16>
@@ -192,10 +233,6 @@ hipError_t launch(const Shape& s, const void* q, const void* k, int8_t* q_i8, fl
                   void* workspace, hipStream_t stream) {
   const int nchunk = s.nchunk();
   double2* part = static_cast<double2*>(workspace);
-  hipLaunchKernelGGL((ksum_partial_kernel<D, BF16>), dim3(nchunk, s.B * s.Hkv), dim3(kThreads), 0,
-                     stream, static_cast<const uint16_t*>(k), part, s.N, nchunk);
-  hipLaunchKernelGGL(kmean_finalize_kernel, dim3(s.B * s.Hkv), dim3(128), 0, stream, part, k_mean,
-                     s.N, nchunk, D);
   QuantArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -210,8 +247,13 @@ hipError_t launch(const Shape& s, const void* q, const void* k, int8_t* q_i8, fl
   a.nqb = s.nqb();
   a.nkb = s.nkb();
   a.nQ = s.B * s.Hq * a.nqb;
+  const int nsum = s.B * s.Hkv * nchunk;
   const int nK = s.B * s.Hkv * a.nkb;
-  hipLaunchKernelGGL((quant_kernel<D, BF16>), dim3(a.nQ + nK), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((ksum_qquant_kernel<D, BF16>), dim3(nsum + a.nQ), dim3(kThreads), 0, stream,
+                     a, part, nchunk, nsum);
+  hipLaunchKernelGGL(kmean_finalize_kernel, dim3(s.B * s.Hkv, D / kFinChans),
+                     dim3(kFinGroups * kFinChans), 0, stream, part, k_mean, s.N, nchunk, D);
+  hipLaunchKernelGGL((kquant_kernel<D, BF16>), dim3(nK), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

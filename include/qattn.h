@@ -170,8 +170,9 @@ qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool,
  *   alpha = fl32(fl32(q_scale * fl32(log2(e)/sqrt(d))) * k_scale);
  *   s = S * alpha, -inf where the key is masked;
  *   c = max(m, rowmax s); m' = c if c > m + QATTN_SOFTMAX_REF_THRESHOLD
- *   (or m = -inf), else m' = m; P = exp2(s - m') rounded to V's dtype;
- *   l = l * exp2(m - m') + rowsum P; acc = acc * exp2(m - m') + P V (fp32);
+ *   (or m = -inf), else m' = m; P = exp2(s - m'), P_hat = P rounded to V's
+ *   dtype; l = l * exp2(m - m') + rowsum P (before the rounding);
+ *   acc = acc * exp2(m - m') + P_hat V (fp32);
  *   O = acc / l rounded to V's dtype; lse = ln2 * (m + log2 l), the natural
  *   log-sum-exp of the smoothed, dequantized logits (S * alpha / log2(e)).
  * In:  q_i8, q_scale, k_i8, k_scale as written by qattn_smooth_quant;

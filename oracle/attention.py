@@ -28,8 +28,11 @@ where the pages are silent:
 * P = fl32(exp2(fl32(s - m_new))); P_hat = P rounded to nearest-even in V's
   dtype (the 16-bit operand of the P V product);
   corr = fl32(exp2(fl32(m_old - m_new))) (1 when the reference did not move);
-  l = l * corr + sum(P_hat); acc = acc * corr + P_hat V, accumulated in fp64
-  (the kernel accumulates in fp32: the 16-bit products are exact in either);
+  l = l * corr + sum(P), the row sum of P before its 16-bit rounding, as in
+  FlashAttention-2's online softmax; acc = acc * corr + P_hat V, accumulated
+  in fp64 (the kernel accumulates in fp32: the 16-bit products are exact in
+  either). With V = 1 the output is sum(P_hat) / sum(P), within the unit
+  roundoff of V's dtype of 1;
 * O = round_dtype(fl32(acc / l)); lse = ln(2) * (m + log2(l)), the natural log
   normalizer of the smoothed, dequantized logits.
 """
@@ -182,7 +185,7 @@ def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hk
             dm = np.where(np.isfinite(m), (m - np.where(live, m_new, 0)).astype(np.float32), ninf)
             corr = np.where(np.isfinite(m), np.exp2(dm.astype(np.float64)).astype(np.float32), 0.0)
             corr = np.where(live, corr, 1.0).astype(np.float64)
-            l = l * corr + P_hat.sum(axis=1)
+            l = l * corr + P.astype(np.float64).sum(axis=1)
             acc = acc * corr[:, None] + P_hat @ v64[b, hk, k0:k0 + kv_tile]
             m = m_new
         with np.errstate(invalid="ignore", divide="ignore"):

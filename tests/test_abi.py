@@ -150,9 +150,9 @@ def test_max_keep_and_workspace_sizes(lib):
     assert qa.qattn_max_keep(p, 0, 1) == 3
     assert qa.qattn_max_keep(p, 2, 1) == -1
     ws = qa.qattn_workspace_bytes(p)
-    # K partial sums: 8 heads x 64 chunks x 128 channels x 16 bytes; mask codes:
+    # K partial sums: 8 heads x 256 chunks x 128 channels x 16 bytes; mask codes:
     # (32*256 + 8*512) pooled vectors x (128 + 4) bytes
-    assert ws == max(8 * 64 * 128 * 16, (32 * 256 + 8 * 512) * 132)
+    assert ws == max(8 * 256 * 128 * 16, (32 * 256 + 8 * 512) * 132)
 
 
 def test_binding_has_the_c_names():
