@@ -25,18 +25,21 @@
 // conflicts. The V^T operand comes from ds_read_b64_tr_b16, which hands each
 // lane 4 consecutive keys of one channel.
 //
-// Pipeline (three K/V buffers, one barrier per tile): each wave runs S, the
-// softmax and P V of its tile in sequence; the waves sharing a SIMD overlap
-// each other's matrix and vector work. The loads of the tile two ahead go out
-// once the current S products are queued. Dense workgroups keep each wave's Q
-// fragments in LDS; every K tile carries its scale in a small tail of its LDS
-// buffer (no scalar loads in the loop).
+// Pipeline (one barrier per tile; each stage of K tile, its scale and V tile
+// is one LDS object): dense workgroups run the P V products of tile t-1
+// inside the softmax of tile t, so each wave feeds its matrix unit while its
+// vector unit works (four stages); sparse workgroups run S, the softmax and
+// P V of a tile in sequence (three stages) and the waves sharing a SIMD
+// overlap each other's work. Q fragments stay in registers; every K tile
+// carries its scale in a small tail of its stage (no scalar loads in the
+// loop).
 //
 // Online softmax reference: a row's exponent reference m moves only when the
 // tile's running max exceeds it by more than kTau (log2 units); otherwise P is
 // taken against the stale reference (P <= 2^kTau) and the accumulator is not
-// rescaled. The move test is wave-uniform, so the rescale is skipped for the
-// whole wave in the common case.
+// rescaled. The row max is only formed when a partial row sum says a move is
+// possible; the move test is wave-uniform, so the common case costs neither
+// the max nor the rescale.
 #include <climits>
 #include <type_traits>
 
@@ -170,6 +173,12 @@ void attn_fwd_kernel(FwdArgs a) {
   using el_t = typename MM::el_t;
   using G = Geo<D>;
   constexpr int RW = 32 * QB;
+  // lagged P V (dense); two-stage: S of tile t+1 also runs inside the softmax
+  // of tile t (its registers leave no room for the biased-S constant)
+  constexpr bool kLAG = !SPARSE && NW * QB >= 8;
+  constexpr bool kLAG2 = kLAG && NBUF == 6;
+  static_assert(!kLAG2 || QB == 1, "two-stage pipeline: one query block per wave");
+  constexpr bool kBIAS = !kLAG2;
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
   // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
@@ -178,29 +187,26 @@ void attn_fwd_kernel(FwdArgs a) {
   // landing in another, and waits only for the loads of the buffer it reads.
   // (Its tracking has room for few objects; one per stage keeps every read of
   // the loop clear of the loads in flight.)
-  static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
+  static_assert(NBUF >= 3 && NBUF <= 6, "three to six staging buffers");
   constexpr int KB = G::KBUF + 256;  // K tile plus the tail carrying its scale
   constexpr int SB = KB + G::VBUF;   // one stage
   __shared__ __attribute__((aligned(16))) int8_t stage0[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage1[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage2[SB];
-  __shared__ __attribute__((aligned(16))) int8_t stage3[NBUF == 4 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) int8_t stage3[NBUF > 3 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) int8_t stage4[NBUF > 4 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) int8_t stage5[NBUF > 5 ? SB : 16];
   auto stage = [&](auto i) -> int8_t* {
     constexpr int j = decltype(i)::value % NBUF;
     if constexpr (j == 0) return stage0;
     else if constexpr (j == 1) return stage1;
     else if constexpr (j == 2) return stage2;
-    else return stage3;
+    else if constexpr (j == 3) return stage3;
+    else if constexpr (j == 4) return stage4;
+    else return stage5;
   };
   auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
-  // Dense workgroups keep each wave's Q fragments in LDS (same swizzle as a
-  // K block) and read them per tile: that frees the 16 registers they would
-  // hold for the whole kernel. Sparse workgroups keep them in registers (their
-  // LDS budget allows two workgroups per CU).
-  constexpr bool QL = !SPARSE;
-  static_assert(!QL || QB == 1, "Q in LDS takes one 32-row block per wave");
-  __shared__ __attribute__((aligned(16))) int8_t q_lds[QL ? NW * 32 * D : 16];
   __shared__ int16_t tile_list[SPARSE ? kMaxSparseTiles : 1];
   __shared__ int n_list, n_list_plain;
 
@@ -376,14 +382,14 @@ void attn_fwd_kernel(FwdArgs a) {
   int k_frag_off[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
-  const int8_t* q_wave = q_lds + (QL ? wave * 32 * D : 0);
-  // (held in registers for the whole loop: the empty asm hides the constant,
-  // so it is not rematerialized with 16 moves per tile)
+  // Initial accumulator of the S products: the bias pattern, held in
+  // registers for the whole loop (the empty asm hides the constant, so it is
+  // not rematerialized with 16 moves per tile), or zero.
   v16i sbias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    int bv = kSBias;
-    asm volatile("" : "+v"(bv));
+    int bv = kBIAS ? kSBias : 0;
+    if constexpr (kBIAS) asm volatile("" : "+v"(bv));
     sbias[r] = bv;
   }
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
@@ -391,10 +397,7 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int ks = 0; ks < G::KS; ++ks) {
       v4i qv[QB];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        if constexpr (QL) qv[qb] = *reinterpret_cast<const v4i*>(q_wave + k_frag_off[ks]);
-        else qv[qb] = qf[qb][ks];
-      }
+      for (int qb = 0; qb < QB; ++qb) qv[qb] = qf[qb][ks];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const v4i kf = *reinterpret_cast<const v4i*>(kbuf + kb * 32 * G::KROW + k_frag_off[ks]);
@@ -407,6 +410,28 @@ void attn_fwd_kernel(FwdArgs a) {
           }
         }
       }
+    }
+  };
+
+  // The S products in four groups (two per group for d = 128, one for
+  // d = 64): product idx = g*QKG + m is k-step idx/2 of key block idx%2.
+  constexpr int QKG = G::KS * 2 / 4;
+  auto load_kgrp = [&](const int8_t* kbuf, int g, v4i (&kf)[QKG]) {
+#pragma unroll
+    for (int m = 0; m < QKG; ++m) {
+      const int idx = g * QKG + m;
+      kf[m] = *reinterpret_cast<const v4i*>(kbuf + (idx & 1) * 32 * G::KROW + k_frag_off[idx >> 1]);
+    }
+  };
+  auto qk_grp = [&](const v4i (&kf)[QKG], int g, v16i (&s)[2][QB]) {
+#pragma unroll
+    for (int m = 0; m < QKG; ++m) {
+      const int idx = g * QKG + m;
+      const int ks = idx >> 1, kb = idx & 1;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[m], qf[qb][ks],
+                                                          ks == 0 ? sbias : s[kb][qb], 0, 0, 0);
     }
   };
 
@@ -424,33 +449,39 @@ void attn_fwd_kernel(FwdArgs a) {
   // against the new reference, and acc and l are rescaled (corr). With
   // MASKED (causal tiles reaching past the workgroup's first row), element
   // (kb, r), which holds key t*64 + 4h + off, is dropped when off > lim.
-  // hook(g) runs at the start of group g = 2*kb + half of the first pass
-  // (the lagged P V products of the previous tile interleave there).
+  // hook(qb, g) runs at the start of group g = 2*kb + half of the first pass
+  // over query block qb (the lagged P V products of the previous tile
+  // interleave there).
   auto softmax = [&](auto masked_c, const v16i (&s)[2][QB], float alpha, int t,
                      op_t (&pf)[2][QB][2], auto&& hook) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const float a_hi = alpha * kSBiasF;
     const float a_lo = __builtin_fmaf(alpha, kSBiasF, -a_hi);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    static_for<0, QB>([&](auto qbc) {
+      constexpr int qb = decltype(qbc)::value;
       const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
       // P against reference m (-inf: every visible P is +inf, which forces
       // the row max below), and its partial sum
-      auto exps = [&](float m, float ahi, auto&& grp_hook) -> float {
+      auto exps = [&](float m, float ahi, int sofs, auto&& grp_hook) -> float {
         const float cm = m + a_lo;
         float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         static_for<0, 4>([&](auto gc) {
           constexpr int kb = decltype(gc)::value >> 1;
           constexpr int half = decltype(gc)::value & 1;
-          grp_hook(gc);
+          grp_hook(qbc, gc);
           {
             op_t pk;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * half + e;
               const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-              const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
-              const float x = __builtin_fmaf(alpha, sb, -ahi) - cm;
+              float x;
+              if constexpr (kBIAS) {
+                const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
+                x = __builtin_fmaf(alpha, sb, -ahi) - cm;
+              } else {
+                x = __builtin_fmaf((float)((int)s[kb][qb][r] + sofs), alpha, -m);
+              }
               float pe = __builtin_amdgcn_exp2f(x);
               if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
               lsum[e & 3] += pe;
@@ -461,7 +492,7 @@ void attn_fwd_kernel(FwdArgs a) {
         });
         return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
       };
-      float psum = exps(m_ref[qb], a_hi, hook);
+      float psum = exps(m_ref[qb], a_hi, 0, hook);
       if (__ballot(psum > kSumFilter) != 0) {
         // row max over the lane's 32 keys (biased integers; masked keys
         // excluded), then over the other half-row
@@ -487,7 +518,8 @@ void attn_fwd_kernel(FwdArgs a) {
           mxi = max((int)sw[0], (int)sw[1]);
         }
         // fl32(max S * alpha); -inf for a fully masked row, which never moves
-        const float mx = mxi == INT_MIN ? -__builtin_inff() : (float)(mxi - kSBias) * alpha;
+        const float mx =
+            mxi == INT_MIN ? -__builtin_inff() : (float)(mxi - (kBIAS ? kSBias : 0)) * alpha;
         const float m_old = m_ref[qb];
         const float mc = __builtin_fmaxf(m_old, mx);
         const bool move = mc > m_old + kTau;
@@ -498,8 +530,9 @@ void attn_fwd_kernel(FwdArgs a) {
           // recompute from S (an opaque copy of a_hi keeps the compiler from
           // holding the 32 first-pass products live across the fast path)
           float ahi = a_hi;
-          asm volatile("" : "+v"(ahi));
-          psum = exps(m_ref[qb], ahi, [](auto) {});
+          int sofs = 0;
+          asm volatile("" : "+v"(ahi), "+v"(sofs));
+          psum = exps(m_ref[qb], ahi, sofs, [](auto, auto) {});
           l_run[qb] *= corr;
 #pragma unroll
           for (int db = 0; db < G::DB; ++db)
@@ -508,7 +541,7 @@ void attn_fwd_kernel(FwdArgs a) {
         }
       }
       l_run[qb] += psum;
-    }
+    });
   };
 
   // transposing V reads: 16-lane group g = lane/16 reads key rows
@@ -578,9 +611,10 @@ void attn_fwd_kernel(FwdArgs a) {
   // by a zero P). V(it-1) is still read in iteration it, so the prefetch distance is
   // NBUF-2. Otherwise (sparse) each wave runs S, the softmax and P V of a
   // tile in sequence and the waves sharing a SIMD overlap each other's work.
-  constexpr bool kLAG = !SPARSE && NW == 8;
-  static_assert(!kLAG || NBUF == 4, "the lagged products keep four staging buffers");
-  constexpr int PD = kLAG ? NBUF - 2 : NBUF - 1;  // prefetch distance (tiles)
+  static_assert(!kLAG || NBUF == 4 || NBUF == 6, "lagged products: four or six stages");
+  // prefetch distance (tiles) and the furthest tile the next iteration reads
+  constexpr int PD = kLAG2 ? 3 : kLAG ? NBUF - 2 : NBUF - 1;
+  constexpr int AHEAD = kLAG2 ? 2 : 1;
   static_for<0, PD>([&](auto j) {
     const int tt = tile_of(min((int)j, ntiles - 1));
     load_k(tt, kbuf(j));
@@ -591,25 +625,26 @@ void attn_fwd_kernel(FwdArgs a) {
   // time: a runtime choice of LDS buffer makes the compiler wait for every
   // load in flight before reading it)
   if constexpr (kLAG) load_v(tile_of(0), vbuf(std::integral_constant<int, NBUF - 1>{}));
-  if constexpr (QL) {
-    // this wave's Q fragments into its LDS slot (row l32, chunk 2ks+h,
-    // swizzled like a K block)
-    if (wave_live) {
-#pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks)
-        *reinterpret_cast<v4i*>(q_lds + wave * 32 * D + k_frag_off[ks]) = qf[0][ks];
-    }
-  }
   wait_all();
   __syncthreads();
 
   constexpr int kLoadsPerIt = KPW + 1 + VPW;  // K pieces, the K scale, V pieces
   constexpr auto vmcnt = [](int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); };
-  static_assert((PD - 1) * kLoadsPerIt < 64, "vmcnt range");
+  static_assert((PD - AHEAD) * kLoadsPerIt < 64, "vmcnt range");
   constexpr std::integral_constant<bool, true> kYes{};
   constexpr std::integral_constant<bool, false> kNo{};
 
   op_t p_even[2][QB][2], p_odd[2][QB][2];  // lagged: P of even / odd tiles
+  v16i s_even[2][QB], s_odd[2][QB];        // two-stage: S of even / odd tiles
+  float alpha_even = 0.0f, alpha_odd = 0.0f;
+  if constexpr (kLAG2) {
+    // S and the scale of tile 0 before the loop
+    if (wave_live) {
+      const std::integral_constant<int, 0> c0{};
+      qk(kbuf(c0), s_even);
+      alpha_even = alpha_q * tile_kscale(kbuf(c0));
+    }
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -630,30 +665,71 @@ void attn_fwd_kernel(FwdArgs a) {
     const int t = tile_of(it);
     v16i s[2][QB];
     float alpha = 0.0f;
-    if constexpr (kLAG) {
+    (void)s;
+    if constexpr (kLAG2) {
+      // S(t) was formed in the previous iteration; this one forms S(t+1)
       // (NBUF is even, so J and it have the same parity)
+      const std::integral_constant<int, (J + 1) % NBUF> nx1{};
       const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
       op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
+      const v16i (&s_in)[2][QB] = (J & 1) ? s_odd : s_even;
+      v16i (&s_out)[2][QB] = (J & 1) ? s_even : s_odd;
+      alpha = (J & 1) ? alpha_odd : alpha_even;
+      float& alpha_nx = (J & 1) ? alpha_even : alpha_odd;
       const int8_t* vp = vbuf(prv);
+      const int8_t* kp = kbuf(nx1);
       op_t va[G::DB], vb[G::DB];
+      v4i kfa[QKG], kfb[QKG];
       if (wave_live) {
-        alpha = alpha_q * tile_kscale(kbuf(cur));
         load_vgrp(vp, 0, va);
         load_vgrp(vp, 1, vb);
-        qk(kbuf(cur), s);
+        load_kgrp(kp, 0, kfa);
+        alpha_nx = alpha_q * tile_kscale(kp);
       }
       load_k(tl, kbuf(nxt));
       load_v(tl, vbuf(nxt));
       if (wave_live) {
-        auto lagged_pv = [&](auto gc) {
+        auto lagged = [&](auto, auto gc) {
           constexpr int g = decltype(gc)::value;
           op_t (&vf)[G::DB] = (g & 1) ? vb : va;
+          v4i (&kf)[QKG] = (g & 1) ? kfb : kfa;
+          v4i (&kf_next)[QKG] = (g & 1) ? kfa : kfb;
 #pragma unroll
           for (int db = 0; db < G::DB; ++db)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               acc[db][qb] = MM::mma(vf[db], p_in[g >> 1][qb][g & 1], acc[db][qb]);
           if constexpr (g + 2 < 4) load_vgrp(vp, g + 2, vf);
+          qk_grp(kf, g, s_out);
+          if constexpr (g + 1 < 4) load_kgrp(kp, g + 1, kf_next);
+        };
+        softmax(masked_c, s_in, alpha, t, p_out, lagged);
+      }
+    } else if constexpr (kLAG) {
+      // (NBUF is even, so J and it have the same parity)
+      const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
+      op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
+      const int8_t* vp = vbuf(prv);
+      // QB = 1: two fragment sets, refilled two groups ahead; QB > 1: all
+      // four groups of V(t-1) at once, each set shared by the QB blocks
+      constexpr int NVS = QB == 1 ? 2 : 4;
+      op_t vset[NVS][G::DB];
+      if (wave_live) {
+        alpha = alpha_q * tile_kscale(kbuf(cur));
+        static_for<0, NVS>([&](auto gc) { load_vgrp(vp, decltype(gc)::value, vset[decltype(gc)::value]); });
+        qk(kbuf(cur), s);
+      }
+      load_k(tl, kbuf(nxt));
+      load_v(tl, vbuf(nxt));
+      if (wave_live) {
+        auto lagged_pv = [&](auto qbc, auto gc) {
+          constexpr int qb = decltype(qbc)::value;
+          constexpr int g = decltype(gc)::value;
+          op_t (&vf)[G::DB] = vset[g % NVS];
+#pragma unroll
+          for (int db = 0; db < G::DB; ++db)
+            acc[db][qb] = MM::mma(vf[db], p_in[g >> 1][qb][g & 1], acc[db][qb]);
+          if constexpr (QB == 1 && g + 2 < 4) load_vgrp(vp, g + 2, vf);
         };
         softmax(masked_c, s, alpha, t, p_out, lagged_pv);
       }
@@ -666,7 +742,7 @@ void attn_fwd_kernel(FwdArgs a) {
       load_v(tl, vbuf(nxt));
       if (wave_live) {
         op_t p[2][QB][2];
-        softmax(masked_c, s, alpha, t, p, [](auto) {});
+        softmax(masked_c, s, alpha, t, p, [](auto, auto) {});
         pv(vbuf(cur), p);
       }
     }
@@ -675,7 +751,7 @@ void attn_fwd_kernel(FwdArgs a) {
     if constexpr (decltype(masked_c)::value) {
       wait_all();
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt((PD - 1) * kLoadsPerIt));
+      __builtin_amdgcn_s_waitcnt(vmcnt((PD - AHEAD) * kLoadsPerIt));
     }
     barrier();
   };
@@ -731,20 +807,30 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+#ifndef QATTN_LAG2
+#define QATTN_LAG2 0
+#endif
+#ifndef QATTN_NW_DENSE64
+#define QATTN_NW_DENSE64 8
+#endif
 #ifndef QATTN_NW_DENSE
 #define QATTN_NW_DENSE 8
 #endif
 #ifndef QATTN_QB
 #define QATTN_QB 1
 #endif
+#ifndef QATTN_QB_DENSE
+#define QATTN_QB_DENSE 1
+#endif
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
-  constexpr int QB = QATTN_QB;  // 32-query blocks per wave
+  constexpr int QB = QATTN_QB;     // 32-query blocks per wave (sparse)
+  constexpr int QBD = QATTN_QB_DENSE;  // 32-query blocks per wave (dense)
   // dense: one workgroup of NW_DENSE waves per CU (NW_DENSE / 4 waves per
-  // SIMD); sparse: one 128-row query block per 4-wave workgroup, two
-  // workgroups per CU
-  constexpr int NW_DENSE = QATTN_NW_DENSE;
+  // SIMD), 8 query blocks of 32 rows in all; sparse: one 128-row query block
+  // per 4-wave workgroup, two workgroups per CU
+  constexpr int NW_DENSE = (D == 64 ? QATTN_NW_DENSE64 : QATTN_NW_DENSE) / QBD;
   constexpr int WPE_DENSE = NW_DENSE / 4;
   constexpr int NW_SPARSE = 128 / (32 * QB);
   static_assert(NW_DENSE % 4 == 0, "whole waves per SIMD");
@@ -753,11 +839,11 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
     hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3>), grid,
                        dim3(NW_SPARSE * 64), 0, stream, a);
   } else {
-    const int rows_wg = 32 * QB * (NW_DENSE / a.g4);
+    const int rows_wg = 32 * QBD * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
-    constexpr int NBUF_DENSE = NW_DENSE == 8 ? 4 : 3;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QB, NW_DENSE, WPE_DENSE, NBUF_DENSE>),
+    constexpr int NBUF_DENSE = NW_DENSE * QBD >= 8 ? (QATTN_LAG2 ? 6 : 4) : 3;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE>),
                        grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();
