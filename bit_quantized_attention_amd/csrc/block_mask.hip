@@ -8,10 +8,12 @@
 //      heads w, w+4, ... of the group. Per chunk of 256 key blocks the
 //      workgroup stages the key codes in LDS; lane l of a wave scores key
 //      blocks l, l+64, ... with v_dot4 (exact int32) and two fp32 roundings.
-//      A 32-pass radix select over the order-preserving integer image of the
-//      scores finds the k-th largest candidate (ties at the threshold go to
-//      the lower block index); ballot/popcount prefix sums write forced and
-//      selected blocks in ascending order and pad with -1.
+//      A radix select over the order-preserving integer image of the scores
+//      (most significant bit first, stopping once the candidates sharing the
+//      prefix are exactly the ones still wanted) finds the k-th largest
+//      candidate (ties at the threshold go to the lower block index);
+//      ballot/popcount prefix sums write forced and selected blocks in
+//      ascending order and pad with -1.
 #include "device_util.h"
 #include "qattn_internal.h"
 
@@ -179,12 +181,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     const int ncand = nvalid - nforced;
     const long long kwant = ((long long)nvalid * a.keep_num + a.keep_den - 1) / a.keep_den;
     const int ksel = (int)(kwant < ncand ? kwant : ncand);
-    uint32_t thr = 0xffffffffu;
+    // Radix select, most significant bit first: after each bit, `prefix`
+    // (under `mask`) is the top bits of the ksel-th largest candidate key,
+    // `remaining` how many of the candidates sharing them are still wanted and
+    // `group` how many share them. The search stops as soon as the whole group
+    // is wanted; a full 32-bit prefix is the key itself (ties: the lower
+    // block indices are taken).
+    uint32_t thr = 0xffffffffu, mask = 0xffffffffu;
     int need = 0;
     if (ksel > 0) {
-      uint32_t prefix = 0, mask = 0;
-      int remaining = ksel;
-      for (int bit = 31; bit >= 0; --bit) {
+      uint32_t prefix = 0;
+      int remaining = ksel, group = ncand;
+      mask = 0;
+      for (int bit = 31; bit >= 0 && group > remaining; --bit) {
         const uint32_t mk = mask | (1u << bit);
         const uint32_t test = prefix | (1u << bit);
         int cnt = 0;
@@ -192,13 +201,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
         for (int u = 0; u < SLOTS; ++u) cnt += __popcll(__ballot(cand[u] && (key[u] & mk) == test));
         if (cnt >= remaining) {
           prefix = test;
+          group = cnt;
         } else {
           remaining -= cnt;
+          group -= cnt;
         }
         mask = mk;
       }
-      thr = prefix;      // image of the ksel-th largest candidate score
-      need = remaining;  // how many candidates equal to it are taken
+      thr = prefix;      // top bits (under mask) of the ksel-th largest candidate
+      need = remaining;  // how many candidates with exactly these bits are taken
     }
     int32_t* out = a.kv_idx + row * a.max_keep;
     int eq_before = 0;
@@ -206,8 +217,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) {
       const int j = lane + 64 * u;
-      const bool gt = ksel > 0 && cand[u] && key[u] > thr;
-      const bool eq = ksel > 0 && cand[u] && key[u] == thr;
+      const bool gt = ksel > 0 && cand[u] && (key[u] & mask) > thr;
+      const bool eq = ksel > 0 && cand[u] && (key[u] & mask) == thr;
       const uint64_t eqb = __ballot(eq);
       const int eq_rank = eq_before + __popcll(eqb & lt_mask);
       eq_before += __popcll(eqb);
