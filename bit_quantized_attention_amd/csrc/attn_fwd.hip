@@ -173,12 +173,8 @@ void attn_fwd_kernel(FwdArgs a) {
   using el_t = typename MM::el_t;
   using G = Geo<D>;
   constexpr int RW = 32 * QB;
-  // lagged P V (dense); two-stage: S of tile t+1 also runs inside the softmax
-  // of tile t (its registers leave no room for the biased-S constant)
+  // lagged P V (dense workgroups)
   constexpr bool kLAG = !SPARSE && NW * QB >= 8;
-  constexpr bool kLAG2 = kLAG && NBUF == 6;
-  static_assert(!kLAG2 || QB == 1, "two-stage pipeline: one query block per wave");
-  constexpr bool kBIAS = !kLAG2;
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
   // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
@@ -187,23 +183,19 @@ void attn_fwd_kernel(FwdArgs a) {
   // landing in another, and waits only for the loads of the buffer it reads.
   // (Its tracking has room for few objects; one per stage keeps every read of
   // the loop clear of the loads in flight.)
-  static_assert(NBUF >= 3 && NBUF <= 6, "three to six staging buffers");
+  static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
   constexpr int KB = G::KBUF + 256;  // K tile plus the tail carrying its scale
   constexpr int SB = KB + G::VBUF;   // one stage
   __shared__ __attribute__((aligned(16))) int8_t stage0[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage1[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage2[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage3[NBUF > 3 ? SB : 16];
-  __shared__ __attribute__((aligned(16))) int8_t stage4[NBUF > 4 ? SB : 16];
-  __shared__ __attribute__((aligned(16))) int8_t stage5[NBUF > 5 ? SB : 16];
   auto stage = [&](auto i) -> int8_t* {
     constexpr int j = decltype(i)::value % NBUF;
     if constexpr (j == 0) return stage0;
     else if constexpr (j == 1) return stage1;
     else if constexpr (j == 2) return stage2;
-    else if constexpr (j == 3) return stage3;
-    else if constexpr (j == 4) return stage4;
-    else return stage5;
+    else return stage3;
   };
   auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
@@ -384,12 +376,12 @@ void attn_fwd_kernel(FwdArgs a) {
   for (int ks = 0; ks < G::KS; ++ks) k_frag_off[ks] = l32 * G::KROW + (((2 * ks + h) ^ G::kswz(l32)) * 16);
   // Initial accumulator of the S products: the bias pattern, held in
   // registers for the whole loop (the empty asm hides the constant, so it is
-  // not rematerialized with 16 moves per tile), or zero.
+  // not rematerialized with 16 moves per tile).
   v16i sbias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    int bv = kBIAS ? kSBias : 0;
-    if constexpr (kBIAS) asm volatile("" : "+v"(bv));
+    int bv = kSBias;
+    asm volatile("" : "+v"(bv));
     sbias[r] = bv;
   }
   auto qk = [&](const int8_t* kbuf, v16i (&s)[2][QB]) {
@@ -410,28 +402,6 @@ void attn_fwd_kernel(FwdArgs a) {
           }
         }
       }
-    }
-  };
-
-  // The S products in four groups (two per group for d = 128, one for
-  // d = 64): product idx = g*QKG + m is k-step idx/2 of key block idx%2.
-  constexpr int QKG = G::KS * 2 / 4;
-  auto load_kgrp = [&](const int8_t* kbuf, int g, v4i (&kf)[QKG]) {
-#pragma unroll
-    for (int m = 0; m < QKG; ++m) {
-      const int idx = g * QKG + m;
-      kf[m] = *reinterpret_cast<const v4i*>(kbuf + (idx & 1) * 32 * G::KROW + k_frag_off[idx >> 1]);
-    }
-  };
-  auto qk_grp = [&](const v4i (&kf)[QKG], int g, v16i (&s)[2][QB]) {
-#pragma unroll
-    for (int m = 0; m < QKG; ++m) {
-      const int idx = g * QKG + m;
-      const int ks = idx >> 1, kb = idx & 1;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[kb][qb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[m], qf[qb][ks],
-                                                          ks == 0 ? sbias : s[kb][qb], 0, 0, 0);
     }
   };
 
@@ -462,7 +432,7 @@ void attn_fwd_kernel(FwdArgs a) {
       const int lim = (row0 + 32 * qb + l32) - (t * kKT + 4 * h);
       // P against reference m (-inf: every visible P is +inf, which forces
       // the row max below), and its partial sum
-      auto exps = [&](float m, float ahi, int sofs, auto&& grp_hook) -> float {
+      auto exps = [&](float m, float ahi, auto&& grp_hook) -> float {
         const float cm = m + a_lo;
         float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         static_for<0, 4>([&](auto gc) {
@@ -475,13 +445,8 @@ void attn_fwd_kernel(FwdArgs a) {
             for (int e = 0; e < 8; ++e) {
               const int r = 8 * half + e;
               const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-              float x;
-              if constexpr (kBIAS) {
-                const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
-                x = __builtin_fmaf(alpha, sb, -ahi) - cm;
-              } else {
-                x = __builtin_fmaf((float)((int)s[kb][qb][r] + sofs), alpha, -m);
-              }
+              const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
+              const float x = __builtin_fmaf(alpha, sb, -ahi) - cm;
               float pe = __builtin_amdgcn_exp2f(x);
               if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
               lsum[e & 3] += pe;
@@ -492,7 +457,7 @@ void attn_fwd_kernel(FwdArgs a) {
         });
         return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
       };
-      float psum = exps(m_ref[qb], a_hi, 0, hook);
+      float psum = exps(m_ref[qb], a_hi, hook);
       if (__ballot(psum > kSumFilter) != 0) {
         // row max over the lane's 32 keys (biased integers; masked keys
         // excluded), then over the other half-row
@@ -518,8 +483,7 @@ void attn_fwd_kernel(FwdArgs a) {
           mxi = max((int)sw[0], (int)sw[1]);
         }
         // fl32(max S * alpha); -inf for a fully masked row, which never moves
-        const float mx =
-            mxi == INT_MIN ? -__builtin_inff() : (float)(mxi - (kBIAS ? kSBias : 0)) * alpha;
+        const float mx = mxi == INT_MIN ? -__builtin_inff() : (float)(mxi - kSBias) * alpha;
         const float m_old = m_ref[qb];
         const float mc = __builtin_fmaxf(m_old, mx);
         const bool move = mc > m_old + kTau;
@@ -530,9 +494,8 @@ void attn_fwd_kernel(FwdArgs a) {
           // recompute from S (an opaque copy of a_hi keeps the compiler from
           // holding the 32 first-pass products live across the fast path)
           float ahi = a_hi;
-          int sofs = 0;
-          asm volatile("" : "+v"(ahi), "+v"(sofs));
-          psum = exps(m_ref[qb], ahi, sofs, [](auto, auto) {});
+          asm volatile("" : "+v"(ahi));
+          psum = exps(m_ref[qb], ahi, [](auto, auto) {});
           l_run[qb] *= corr;
 #pragma unroll
           for (int db = 0; db < G::DB; ++db)
@@ -613,8 +576,7 @@ void attn_fwd_kernel(FwdArgs a) {
   // tile in sequence and the waves sharing a SIMD overlap each other's work.
   static_assert(!kLAG || NBUF == 4 || NBUF == 6, "lagged products: four or six stages");
   // prefetch distance (tiles) and the furthest tile the next iteration reads
-  constexpr int PD = kLAG2 ? 3 : kLAG ? NBUF - 2 : NBUF - 1;
-  constexpr int AHEAD = kLAG2 ? 2 : 1;
+  constexpr int PD = kLAG ? NBUF - 2 : NBUF - 1;
   static_for<0, PD>([&](auto j) {
     const int tt = tile_of(min((int)j, ntiles - 1));
     load_k(tt, kbuf(j));
@@ -630,21 +592,12 @@ void attn_fwd_kernel(FwdArgs a) {
 
   constexpr int kLoadsPerIt = KPW + 1 + VPW;  // K pieces, the K scale, V pieces
   constexpr auto vmcnt = [](int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); };
-  static_assert((PD - AHEAD) * kLoadsPerIt < 64, "vmcnt range");
+  static_assert((PD - 1) * kLoadsPerIt < 64, "vmcnt range");
   constexpr std::integral_constant<bool, true> kYes{};
   constexpr std::integral_constant<bool, false> kNo{};
 
-  op_t p_even[2][QB][2], p_odd[2][QB][2];  // lagged: P of even / odd tiles
-  v16i s_even[2][QB], s_odd[2][QB];        // two-stage: S of even / odd tiles
-  float alpha_even = 0.0f, alpha_odd = 0.0f;
-  if constexpr (kLAG2) {
-    // S and the scale of tile 0 before the loop
-    if (wave_live) {
-      const std::integral_constant<int, 0> c0{};
-      qk(kbuf(c0), s_even);
-      alpha_even = alpha_q * tile_kscale(kbuf(c0));
-    }
-  }
+  // lagged: P of even / odd tiles; the "previous" P of the first tile is zero
+  op_t p_even[2][QB][2], p_odd[2][QB][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -665,47 +618,7 @@ void attn_fwd_kernel(FwdArgs a) {
     const int t = tile_of(it);
     v16i s[2][QB];
     float alpha = 0.0f;
-    (void)s;
-    if constexpr (kLAG2) {
-      // S(t) was formed in the previous iteration; this one forms S(t+1)
-      // (NBUF is even, so J and it have the same parity)
-      const std::integral_constant<int, (J + 1) % NBUF> nx1{};
-      const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
-      op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
-      const v16i (&s_in)[2][QB] = (J & 1) ? s_odd : s_even;
-      v16i (&s_out)[2][QB] = (J & 1) ? s_even : s_odd;
-      alpha = (J & 1) ? alpha_odd : alpha_even;
-      float& alpha_nx = (J & 1) ? alpha_even : alpha_odd;
-      const int8_t* vp = vbuf(prv);
-      const int8_t* kp = kbuf(nx1);
-      op_t va[G::DB], vb[G::DB];
-      v4i kfa[QKG], kfb[QKG];
-      if (wave_live) {
-        load_vgrp(vp, 0, va);
-        load_vgrp(vp, 1, vb);
-        load_kgrp(kp, 0, kfa);
-        alpha_nx = alpha_q * tile_kscale(kp);
-      }
-      load_k(tl, kbuf(nxt));
-      load_v(tl, vbuf(nxt));
-      if (wave_live) {
-        auto lagged = [&](auto, auto gc) {
-          constexpr int g = decltype(gc)::value;
-          op_t (&vf)[G::DB] = (g & 1) ? vb : va;
-          v4i (&kf)[QKG] = (g & 1) ? kfb : kfa;
-          v4i (&kf_next)[QKG] = (g & 1) ? kfa : kfb;
-#pragma unroll
-          for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              acc[db][qb] = MM::mma(vf[db], p_in[g >> 1][qb][g & 1], acc[db][qb]);
-          if constexpr (g + 2 < 4) load_vgrp(vp, g + 2, vf);
-          qk_grp(kf, g, s_out);
-          if constexpr (g + 1 < 4) load_kgrp(kp, g + 1, kf_next);
-        };
-        softmax(masked_c, s_in, alpha, t, p_out, lagged);
-      }
-    } else if constexpr (kLAG) {
+    if constexpr (kLAG) {
       // (NBUF is even, so J and it have the same parity)
       const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
       op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
@@ -751,7 +664,7 @@ void attn_fwd_kernel(FwdArgs a) {
     if constexpr (decltype(masked_c)::value) {
       wait_all();
     } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt((PD - AHEAD) * kLoadsPerIt));
+      __builtin_amdgcn_s_waitcnt(vmcnt((PD - 1) * kLoadsPerIt));
     }
     barrier();
   };
@@ -807,9 +720,6 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
-#ifndef QATTN_LAG2
-#define QATTN_LAG2 0
-#endif
 #ifndef QATTN_NW_DENSE64
 #define QATTN_NW_DENSE64 8
 #endif
@@ -842,7 +752,7 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
     const int rows_wg = 32 * QBD * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
-    constexpr int NBUF_DENSE = NW_DENSE * QBD >= 8 ? (QATTN_LAG2 ? 6 : 4) : 3;
+    constexpr int NBUF_DENSE = NW_DENSE * QBD >= 8 ? 4 : 3;
     hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE>),
                        grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
