@@ -16,6 +16,9 @@ written for reading, not for speed:
   keep list.
 * ``emulate_attention``   -- the quantized path step by step: INT8 scores,
   online base-2 softmax, rounded probabilities, fp64 accumulation.
+* ``emulate_promoted_attention`` / ``promote_plan`` -- promote instead of
+  skip: the kept blocks at 16-bit Q K^T, every other visible block through
+  the INT8 path, merged by the same online softmax.
 
 Sources (the explainer pages these follow):
 
@@ -40,4 +43,5 @@ from .rounding import bf16_rne, f16_rne, round_to_dtype  # noqa: F401
 from .quant import (k_channel_mean, quantize_block, smooth_quant,  # noqa: F401
                     pool_vector_quant)
 from .mask import block_mask, max_keep, select_blocks  # noqa: F401
-from .attention import exact_attention, emulate_attention, softmax_scale_log2  # noqa: F401
+from .attention import (exact_attention, emulate_attention, emulate_promoted_attention,  # noqa: F401
+                        promote_plan, softmax_scale_log2)

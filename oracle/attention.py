@@ -106,6 +106,53 @@ def _kv_tiles_dense(i: int, N: int, causal: bool, kv_tile: int):
     return list(range(min(n_tiles, last_key // kv_tile + 1)))
 
 
+def _dtypes(v, p_dtype, out_dtype):
+    """P's and O's rounding dtypes, defaulting to V's 16-bit dtype."""
+    vdt = None
+    try:
+        import torch
+        if isinstance(v, torch.Tensor):
+            vdt = {torch.bfloat16: "bf16", torch.float16: "f16"}.get(v.dtype)
+    except ImportError:  # pragma: no cover
+        pass
+    p_dtype = p_dtype or vdt
+    out_dtype = out_dtype or vdt
+    if p_dtype is None or out_dtype is None:
+        raise ValueError("p_dtype/out_dtype needed when V is not a 16-bit torch tensor")
+    return p_dtype, out_dtype
+
+
+def _online_step(m, l, acc, s, vt, p_dtype, tau):
+    """One step of the online softmax over a tile of fp32 base-2 logits.
+
+    m [rows] f32 reference, l [rows] f64 row sums, acc [rows, d] f64;
+    s [rows, keys] f32 logits (-inf where masked); vt [keys, d] f64 values.
+    The reference rule, P, P_hat, corr, l and acc as in the module docstring.
+    """
+    ninf = np.float32(-np.inf)
+    m_cand = np.maximum(m, s.max(axis=1))
+    move = m_cand > (m + np.float32(tau)).astype(np.float32)
+    m_new = np.where(move, m_cand, m).astype(np.float32)
+    live = np.isfinite(m_new)
+    arg = np.where(live[:, None], (s - np.where(live, m_new, 0)[:, None]).astype(np.float32), ninf)
+    P = np.exp2(arg.astype(np.float64)).astype(np.float32)
+    P_hat = round_to_dtype(P, p_dtype).astype(np.float64)
+    dm = np.where(np.isfinite(m), (m - np.where(live, m_new, 0)).astype(np.float32), ninf)
+    corr = np.where(np.isfinite(m), np.exp2(dm.astype(np.float64)).astype(np.float32), 0.0)
+    corr = np.where(live, corr, 1.0).astype(np.float64)
+    l = l * corr + P.astype(np.float64).sum(axis=1)
+    acc = acc * corr[:, None] + P_hat @ vt
+    return m_new, l, acc
+
+
+def _finish(m, l, acc):
+    """O before its final rounding (f32) and lse (f64) from the final state."""
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o32 = np.where(l[:, None] > 0, acc / l[:, None], 0.0).astype(np.float32)
+        lse = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(l)), -np.inf)
+    return o32, lse
+
+
 def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hkv: int,
                       kv_idx=None, kv_cnt=None, kv_tile: int = K_BLOCK,
                       p_dtype: str | None = None, out_dtype: str | None = None,
@@ -125,17 +172,7 @@ def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hk
     [B,Hq,N,d] f32, lse [B,Hq,N] f64). ``blocks`` restricts the work to a list
     of (b, hq, i); other entries are NaN.
     """
-    vdt = None
-    try:
-        import torch
-        if isinstance(v, torch.Tensor):
-            vdt = {torch.bfloat16: "bf16", torch.float16: "f16"}.get(v.dtype)
-    except ImportError:  # pragma: no cover
-        pass
-    p_dtype = p_dtype or vdt
-    out_dtype = out_dtype or vdt
-    if p_dtype is None or out_dtype is None:
-        raise ValueError("p_dtype/out_dtype needed when V is not a 16-bit torch tensor")
+    p_dtype, out_dtype = _dtypes(v, p_dtype, out_dtype)
     v64 = _as_f64(v)
     B, _, N, d = q_i8.shape
     group = Hq // Hkv
@@ -175,23 +212,104 @@ def emulate_attention(q_i8, q_scale, k_i8, k_scale, v, causal: bool, Hq: int, Hk
             s = (S.astype(np.float32) * alpha[None, :]).astype(np.float32)
             if causal:
                 s = np.where(keys[None, :] <= rows[:, None], s, ninf)
-            m_cand = np.maximum(m, s.max(axis=1))
-            move = m_cand > (m + np.float32(tau)).astype(np.float32)
-            m_new = np.where(move, m_cand, m).astype(np.float32)
-            live = np.isfinite(m_new)
-            arg = np.where(live[:, None], (s - np.where(live, m_new, 0)[:, None]).astype(np.float32), ninf)
-            P = np.exp2(arg.astype(np.float64)).astype(np.float32)
-            P_hat = round_to_dtype(P, p_dtype).astype(np.float64)
-            dm = np.where(np.isfinite(m), (m - np.where(live, m_new, 0)).astype(np.float32), ninf)
-            corr = np.where(np.isfinite(m), np.exp2(dm.astype(np.float64)).astype(np.float32), 0.0)
-            corr = np.where(live, corr, 1.0).astype(np.float64)
-            l = l * corr + P.astype(np.float64).sum(axis=1)
-            acc = acc * corr[:, None] + P_hat @ v64[b, hk, k0:k0 + kv_tile]
-            m = m_new
-        with np.errstate(invalid="ignore", divide="ignore"):
-            o32 = np.where(l[:, None] > 0, acc / l[:, None], 0.0).astype(np.float32)
-            lse[b, hq, r0:r0 + Q_BLOCK] = np.where(
-                l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(l)), -np.inf)
+            m, l, acc = _online_step(m, l, acc, s, v64[b, hk, k0:k0 + kv_tile], p_dtype, tau)
+        o32, lse[b, hq, r0:r0 + Q_BLOCK] = _finish(m, l, acc)
+        O_pre[b, hq, r0:r0 + Q_BLOCK] = o32
+        O[b, hq, r0:r0 + Q_BLOCK] = round_to_dtype(o32, out_dtype)
+    return O, O_pre, lse
+
+
+def promote_plan(kv_idx_row, cnt: int, i: int, N: int, causal: bool):
+    """The two tile lists of query block i on the promoted path.
+
+    promoted: the distinct entries of the kept list (its first ``cnt``) that
+    name a 64-key block in range and causally visible to the block, ascending;
+    low: every other visible block, ascending. Together they cover each
+    visible block exactly once.
+    """
+    visible = _kv_tiles_dense(i, N, causal, K_BLOCK)
+    vis = set(visible)
+    promoted = sorted({int(j) for j in kv_idx_row[:cnt] if int(j) in vis})
+    low = [t for t in visible if t not in set(promoted)]
+    return low, promoted
+
+
+def emulate_promoted_attention(q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, causal: bool,
+                               Hq: int, Hkv: int, kv_idx, kv_cnt,
+                               p_dtype: str | None = None, out_dtype: str | None = None,
+                               blocks=None, tau: float = 0.0):
+    """Promote instead of skip: the kept blocks at 16-bit Q K^T, the rest INT8.
+
+    The ThriftAttention summary (gist.science/ja/paper/2605.23081), technical
+    summary, method: the top-k block pairs are computed in 16-bit precision,
+    every other pair at low precision, and the two are merged by the online
+    softmax; its implementation paragraph runs the low-precision blocks first
+    and the promoted ones after. Here the low path is the INT8 path of
+    ``emulate_attention`` and the kept list comes from the block mask.
+    Readings where the page is silent:
+
+    * per query block, the low blocks (``promote_plan``) are visited first,
+      ascending, as 64-key tiles exactly as in ``emulate_attention``;
+    * then each promoted block, ascending, as two 32-key halves in order;
+      a half's logits use the original 16-bit q and k and the K mean:
+      s = fl32(c * (q . k - q . k_mean)) with c = fl32(log2(e)/sqrt(d)) and
+      the products and sums exact (fp64 here; the kernel accumulates in
+      fp32). Subtracting q . k_mean puts these logits in the same frame as the
+      smoothed INT8 logits (q . (k - k_mean)); without it the two paths would
+      disagree by a per-row constant;
+    * the online-softmax step of each tile or half, the epilogue and lse are
+      those of ``emulate_attention``.
+
+    q [B,Hq,N,d], k [B,Hkv,N,d] (16-bit torch tensors or fp64 arrays),
+    k_mean [B,Hkv,d] f32 (the smoothing mean); kv_idx [B,Hq,N/128,max_keep],
+    kv_cnt [B,Hq,N/128]. Returns (O, O_pre, lse) as ``emulate_attention``.
+    """
+    p_dtype, out_dtype = _dtypes(v, p_dtype, out_dtype)
+    v64, q64, k64 = _as_f64(v), _as_f64(q), _as_f64(k)
+    mean64 = np.asarray(k_mean, dtype=np.float32).astype(np.float64)
+    B, _, N, d = q_i8.shape
+    group = Hq // Hkv
+    c = softmax_scale_log2(d)
+    c64 = float(c)
+    nqb = N // Q_BLOCK
+    half = K_BLOCK // 2
+    O = np.full((B, Hq, N, d), np.nan, dtype=np.float32)
+    O_pre = np.full((B, Hq, N, d), np.nan, dtype=np.float32)
+    lse = np.full((B, Hq, N), np.nan)
+    if blocks is None:
+        blocks = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(nqb)]
+    ninf = np.float32(-np.inf)
+    for b, hq, i in blocks:
+        hk = hq // group
+        r0 = i * Q_BLOCK
+        rows = np.arange(r0, r0 + Q_BLOCK)
+        qc = q_i8[b, hq, r0:r0 + Q_BLOCK].astype(np.float64)
+        alpha_q = np.float32(np.float32(q_scale[b, hq, i]) * c)
+        m = np.full(Q_BLOCK, ninf, dtype=np.float32)
+        l = np.zeros(Q_BLOCK)
+        acc = np.zeros((Q_BLOCK, d))
+        low, promoted = promote_plan(kv_idx[b, hq, i], int(kv_cnt[b, hq, i]), i, N, causal)
+        for t in low:
+            k0 = t * K_BLOCK
+            keys = np.arange(k0, k0 + K_BLOCK)
+            S = qc @ k_i8[b, hk, k0:k0 + K_BLOCK].astype(np.float64).T
+            alpha = np.float32(alpha_q * np.float32(k_scale[b, hk, t]))
+            s = (S.astype(np.float32) * alpha).astype(np.float32)
+            if causal:
+                s = np.where(keys[None, :] <= rows[:, None], s, ninf)
+            m, l, acc = _online_step(m, l, acc, s, v64[b, hk, k0:k0 + K_BLOCK], p_dtype, tau)
+        qrows = q64[b, hq, r0:r0 + Q_BLOCK]
+        qm = qrows @ mean64[b, hk]                  # q . k_mean per row
+        for t in promoted:
+            for hf in range(2):
+                k0 = t * K_BLOCK + hf * half
+                keys = np.arange(k0, k0 + half)
+                raw = qrows @ k64[b, hk, k0:k0 + half].T
+                s = (c64 * (raw - qm[:, None])).astype(np.float32)
+                if causal:
+                    s = np.where(keys[None, :] <= rows[:, None], s, ninf)
+                m, l, acc = _online_step(m, l, acc, s, v64[b, hk, k0:k0 + half], p_dtype, tau)
+        o32, lse[b, hq, r0:r0 + Q_BLOCK] = _finish(m, l, acc)
         O_pre[b, hq, r0:r0 + Q_BLOCK] = o32
         O[b, hq, r0:r0 + Q_BLOCK] = round_to_dtype(o32, out_dtype)
     return O, O_pre, lse
