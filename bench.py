@@ -1,6 +1,7 @@
 """Benchmark of the quantized attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
+                    [--promote]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -15,6 +16,13 @@ operations per launch (causal: 4*d*H*B*N(N+1)/2; sparse: 4*d*64*rows over the
 kept tiles) over its average launch time, measured with HIP events on the
 launch stream, against the INT8 dense matrix peak. ``cpu_baseline`` times the
 CPU oracle on a bounded sample of the same workload.
+
+With ``--promote`` the attention step is qattn_fwd_promoted: the blocks the
+mask keeps (the workload's keep ratio, else first + diagonal + top 10 %) run at
+16-bit Q K^T and every other visible block through the INT8 path. Its
+algorithmic operations are those of the dense problem (4*d per visible pair),
+of which 2*d per promoted pair and 2*d per pair for P V are 16-bit; the peak
+is the matrix bound of that mix (INT8 and 16-bit work each at its own peak).
 """
 
 from __future__ import annotations
@@ -58,13 +66,14 @@ def kernel_code_hash() -> str:
     return h.hexdigest()
 
 
-def counted_traffic(cfg: int):
+def counted_traffic(cfg: int, promote: bool = False):
     """HBM-side bytes per attn_fwd launch from the committed counter summary of
-    this workload (profiles/attn_fwd_<slug>_traffic.txt): FETCH_SIZE and
+    this workload (profiles/attn_fwd[_promoted]_<slug>_traffic.txt): FETCH_SIZE and
     WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain
     copy of known size. None when there is no summary or when the kernel code
     has changed since the counters were taken (its hash is recorded)."""
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{SLUG[cfg]}_traffic.txt")
+    kind = "attn_fwd_promoted" if promote else "attn_fwd"
+    path = os.path.join(ROOT, "profiles", f"{kind}_{SLUG[cfg]}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -102,6 +111,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--promote", action="store_true",
+                    help="promote the kept blocks to 16-bit Q K^T instead of skipping the rest")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -132,7 +143,7 @@ def sparse_pairs(kv_idx: np.ndarray, kv_cnt: np.ndarray, causal: bool) -> float:
     return float(total)
 
 
-def run_cpu_baseline(p, t, target_s: float):
+def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -153,20 +164,25 @@ def run_cpu_baseline(p, t, target_s: float):
         q = t["q"][b:b + 1, hqs].contiguous()
         k = t["k"][b:b + 1, hk:hk + 1].contiguous()
         v = t["v"][b:b + 1, hk:hk + 1].contiguous()
-        sparse = p.sparse is not None
+        sparse = keep is not None
         sq = oracle.smooth_quant(q, k, pools=sparse)
         idx = cnt = None
         if sparse:
-            num, den = p.sparse
+            num, den = keep
             idx, cnt, _ = oracle.block_mask(sq["q_pool"], sq["k_pool"], len(hqs), 1, p.causal,
                                             num, den)
         for n in range(len(hqs)):
             blocks = [(0, n, i) for i in range(nqb)]
-            oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], v,
-                                     p.causal, len(hqs), 1, kv_idx=idx, kv_cnt=cnt,
-                                     blocks=blocks)
+            if promote:
+                oracle.emulate_promoted_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
+                                                  sq["k_scale"], q, k, sq["k_mean"], v, p.causal,
+                                                  len(hqs), 1, idx, cnt, blocks=blocks)
+            else:
+                oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], v,
+                                         p.causal, len(hqs), 1, kv_idx=idx, kv_cnt=cnt,
+                                         blocks=blocks)
             heads_done += 1
-            if sparse:
+            if sparse and not promote:
                 done_ops += 4.0 * p.d * sparse_pairs(idx[:, n:n + 1], cnt[:, n:n + 1], p.causal)
             else:
                 pairs = p.N * (p.N + 1) / 2 if p.causal else float(p.N) ** 2
@@ -181,7 +197,8 @@ def run_cpu_baseline(p, t, target_s: float):
         "unit": "TOPS (algorithmic)",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"oracle smooth_quant + {'block_mask + ' if p.sparse else ''}emulate_attention "
+        "sample": f"oracle smooth_quant + {'block_mask + ' if sparse else ''}"
+                  f"{'emulate_promoted_attention' if promote else 'emulate_attention'} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
                   f"({el:.1f} s); numpy BLAS {blas}",
     }
@@ -205,8 +222,9 @@ def main():
     p, t = make_config(args.config)
     dev = torch.device("cuda:0")
     q, k, v = (t[x].to(dev) for x in "qkv")
+    keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
-                   sparse=p.sparse)
+                   sparse=keep, promote=args.promote)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
@@ -225,11 +243,14 @@ def main():
     for s in range(args.steps):
         sq_ev[s][0].record(stream)
         plan.smooth_quant(q, k)
-        if p.sparse is not None:
+        if keep is not None:
             plan.block_mask()
         sq_ev[s][1].record(stream)
         ev[s][0].record(stream)
-        plan.fwd(v, o)
+        if args.promote:
+            plan.fwd_promoted(q, k, v, o)
+        else:
+            plan.fwd(v, o)
         ev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -255,7 +276,19 @@ def main():
     pre_flushed_ms = float(np.median(flushed))
 
     literal = 4.0 * p.N * p.N * p.d * p.Hq * p.B
-    if p.sparse is not None:
+    peak = PEAK_INT8_TOPS
+    promote_info = None
+    if args.promote:
+        # every visible pair: 2*d for Q K^T (INT8, or 16-bit when promoted) and
+        # 2*d for P V (16-bit)
+        alg = dense_algorithmic_ops(p)
+        prom = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
+        ops_16 = alg / 2 + 2.0 * p.d * prom
+        ops_i8 = alg - ops_16
+        peak = alg / (ops_i8 / PEAK_INT8_TOPS + ops_16 / PEAK_BF16_TFLOPS)
+        promote_info = {"keep": list(keep), "promoted_pair_fraction": prom / (alg / (4.0 * p.d)),
+                        "ops_int8_per_launch": ops_i8, "ops_16bit_per_launch": ops_16}
+    elif p.sparse is not None:
         pairs = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
         alg = 4.0 * p.d * pairs
     else:
@@ -276,15 +309,18 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+bf16" if p.dtype == "bf16" else "i8+f16",
         "data": "synthetic (seeded Gaussian Q/K/V with per-channel K offsets and outlier channels)",
-        "config": {"workload": p.name, "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
-                   "causal": p.causal, "sparse": p.sparse, "input_dtype": p.dtype},
+        "config": {"workload": p.name + (" (kept blocks promoted to 16-bit QK^T, the rest INT8)"
+                                         if args.promote else ""),
+                   "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
+                   "causal": p.causal, "sparse": None if args.promote else p.sparse,
+                   "promote": list(keep) if args.promote else None, "input_dtype": p.dtype},
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
-            "peak": PEAK_INT8_TOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_INT8_TOPS,
-            "traffic": counted_traffic(args.config),
+            "frac": achieved / peak,
+            "traffic": counted_traffic(args.config, args.promote),
             "kernel": "attn_fwd",
             "algorithmic_ops_per_launch": alg,
             "avg_launch_ms": fwd_avg,
@@ -294,14 +330,16 @@ def main():
         "fwd_tops_algorithmic": achieved,
         "preprocess_ms": float(pre_ms.mean()),
         "preprocess_gbs_algorithmic": pre_bytes / (float(pre_ms.mean()) * 1e-3) / 1e9
-        if p.sparse is None else None,
+        if keep is None else None,
         "fwd_ms_median": float(np.median(fwd_ms)),
         "smooth_quant_ms_cache_flushed": pre_flushed_ms,
         "smooth_quant_gbs_cache_flushed": pre_bytes / (pre_flushed_ms * 1e-3) / 1e9,
         "blended_mfma_peak_tops": 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS),
     }
+    if promote_info is not None:
+        res["promote"] = promote_info
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds)
+        res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote)
     print(json.dumps(res))
 
 

@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH):
     lib.qattn_block_mask.restype = ctypes.c_int
     lib.qattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.qattn_fwd.restype = ctypes.c_int
+    lib.qattn_fwd_promoted.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.qattn_fwd_promoted.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -177,13 +179,26 @@ def qattn_fwd(p, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt, max_keep, o, l
     return st
 
 
+def qattn_fwd_promoted(p, q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, kv_idx, kv_cnt,
+                       max_keep, o, lse=None, stream=None, check=True) -> int:
+    st = load().qattn_fwd_promoted(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_i8),
+                                   _ptr(k_scale), _ptr(q), _ptr(k), _ptr(k_mean), _ptr(v),
+                                   _ptr(kv_idx), _ptr(kv_cnt), max_keep, _ptr(o), _ptr(lse),
+                                   _stream(stream))
+    if check:
+        _check(st, "qattn_fwd_promoted")
+    return st
+
+
 # ---- convenience: allocate intermediates and chain the calls ----------------------
 
 @dataclass
 class Plan:
     """Intermediates for one problem shape, allocated once on ``device``.
 
-    ``sparse`` is None (dense) or a keep ratio (keep_num, keep_den).
+    ``sparse`` is None (dense) or a keep ratio (keep_num, keep_den). With
+    ``promote`` the kept blocks are computed at 16-bit Q K^T and every other
+    block through the INT8 path, instead of being skipped.
     """
 
     p: qattn_problem_t
@@ -191,9 +206,12 @@ class Plan:
     sparse: Optional[Tuple[int, int]] = None
     with_lse: bool = False
     pools: Optional[bool] = None  # pooled block means; default: only when sparse
+    promote: bool = False
 
     def __post_init__(self):
         import torch
+        if self.promote and self.sparse is None:
+            raise ValueError("promote needs a keep ratio (the blocks to promote)")
         p, dev = self.p, self.device
         B, Hq, Hkv, N, d = p.B, p.Hq, p.Hkv, p.N, p.d
         nqb, nkb = N // Q_BLOCK, N // K_BLOCK
@@ -233,24 +251,37 @@ class Plan:
         qattn_fwd(self.p, self.q_i8, self.q_scale, self.k_i8, self.k_scale, v, self.kv_idx,
                   self.kv_cnt, self.max_keep, o, self.lse, stream=stream)
 
+    def fwd_promoted(self, q, k, v, o, stream=None):
+        qattn_fwd_promoted(self.p, self.q_i8, self.q_scale, self.k_i8, self.k_scale, q, k,
+                           self.k_mean, v, self.kv_idx, self.kv_cnt, self.max_keep, o, self.lse,
+                           stream=stream)
+
     def run(self, q, k, v, o, stream=None):
         """The whole path: smooth + quantize, [block mask], attention."""
         self.smooth_quant(q, k, stream)
         if self.sparse is not None:
             self.block_mask(stream)
-        self.fwd(v, o, stream)
+        if self.promote:
+            self.fwd_promoted(q, k, v, o, stream)
+        else:
+            self.fwd(v, o, stream)
         return o
 
 
 def attention(q, k, v, causal: bool = False, sparse: Optional[Tuple[int, int]] = None,
-              return_plan: bool = False, with_lse: bool = False):
-    """O = attention(Q, K, V) through the quantized path; Q [B,Hq,N,d], K/V [B,Hkv,N,d]."""
+              return_plan: bool = False, with_lse: bool = False, promote: bool = False):
+    """O = attention(Q, K, V) through the quantized path; Q [B,Hq,N,d], K/V [B,Hkv,N,d].
+
+    ``sparse`` = (keep_num, keep_den) keeps the first, diagonal and top blocks
+    per query block and skips the rest; with ``promote`` those blocks run at
+    16-bit Q K^T and the rest through the INT8 path instead.
+    """
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
-    plan = Plan(problem_of(q, k, causal), q.device, sparse, with_lse)
+    plan = Plan(problem_of(q, k, causal), q.device, sparse, with_lse, promote=promote)
     o = torch.empty_like(q)
     plan.run(q, k, v, o)
     return (o, plan) if return_plan else o

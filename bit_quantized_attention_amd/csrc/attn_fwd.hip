@@ -118,6 +118,10 @@ struct FwdArgs {
   float* lse;
   const int32_t* kv_idx;
   const int32_t* kv_cnt;
+  // promoted path: the 16-bit Q and K and the K smoothing mean
+  const uint16_t* q16;
+  const uint16_t* k16;
+  const float* k_mean;
   int B, Hq, Hkv, N, group, g4, nqb, nkb, max_keep;
   float c;  // fl32(log2(e) / sqrt(d))
 };
@@ -140,6 +144,13 @@ struct Geo {
   // Swizzle of a V row: the 32 lanes of one phase read 4 rows x 2 channel
   // halves x 32 bytes; these 8 pieces land on disjoint bank groups.
   static __device__ __forceinline__ int vswz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+  // Promoted tiles: half a tile (32 keys) of the 16-bit K fills the same
+  // KBUF bytes, in rows of 2*D bytes; the 16-bit product takes 16-deep
+  // k-steps. Same swizzle rule as kswz for the longer rows.
+  static constexpr int K16ROW = 2 * D;
+  static constexpr int K16SLOTS = K16ROW / 16;
+  static constexpr int KS16 = D / 16;
+  static __device__ __forceinline__ int k16swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // 16 bytes per lane from global memory straight into LDS at
@@ -164,7 +175,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF, bool PROMOTE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
@@ -175,6 +186,9 @@ void attn_fwd_kernel(FwdArgs a) {
   constexpr int RW = 32 * QB;
   // lagged P V (dense workgroups)
   constexpr bool kLAG = !SPARSE && NW * QB >= 8;
+  // promoted path: sparse layout (one 128-row query block per workgroup),
+  // one 32-query block per wave
+  static_assert(!PROMOTE || (SPARSE && QB == 1), "promoted path: sparse layout, QB = 1");
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
   // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
@@ -200,7 +214,8 @@ void attn_fwd_kernel(FwdArgs a) {
   auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
   __shared__ int16_t tile_list[SPARSE ? kMaxSparseTiles : 1];
-  __shared__ int n_list, n_list_plain;
+  __shared__ uint32_t kept_bits[PROMOTE ? kMaxSparseTiles / 32 : 1];
+  __shared__ int n_list, n_list_plain, n_list_hi;
 
   const int lane = threadIdx.x & 63;
   // wave index as a uniform (scalar) value: branches on it stay uniform
@@ -251,7 +266,55 @@ void attn_fwd_kernel(FwdArgs a) {
   // ascending, this is the given order).
   auto masked = [&](int t) -> bool { return CAUSAL && t * kKT + kKT - 1 > wg_row0; };
   int ntiles, n_plain;
-  if constexpr (SPARSE) {
+  int n_hi = 0;  // promoted tiles (each visited as two 32-key halves)
+  if constexpr (PROMOTE) {
+    // The kept list marks the promoted tiles in a bit set (so duplicates and
+    // order do not matter); one ascending scan of the visible tiles then
+    // writes the low tiles to tile_list[0, n1) and the promoted ones to
+    // tile_list[n1, n1 + n_hi).
+    const int nvis = CAUSAL ? min(a.nkb, wg_last_row / kKT + 1) : a.nkb;
+    const int nwords = (nvis + 31) >> 5;
+    for (int w = threadIdx.x; w < nwords; w += NW * 64) kept_bits[w] = 0u;
+    __syncthreads();
+    {
+      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
+      const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
+      for (int e = threadIdx.x; e < cnt; e += NW * 64) {
+        const int t = src[e];
+        if (t >= 0 && t < nvis) atomicOr(&kept_bits[t >> 5], 1u << (t & 31));
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      auto is_kept = [&](int t) { return t < nvis && ((kept_bits[t >> 5] >> (t & 31)) & 1u) != 0u; };
+      int nk = 0;
+      for (int t0 = 0; t0 < nvis; t0 += 64) nk += __popcll(__ballot(is_kept(t0 + lane)));
+      const int n1 = nvis - nk;
+      int p1 = 0, p2 = 0, p1_plain = 0;
+      for (int t0 = 0; t0 < nvis; t0 += 64) {
+        const int t = t0 + lane;
+        const bool kept = is_kept(t);
+        const bool low = t < nvis && !kept;
+        const uint64_t bl = __ballot(low);
+        const uint64_t bk = __ballot(kept);
+        if (low) tile_list[p1 + __popcll(bl & lt)] = (int16_t)t;
+        if (kept) tile_list[n1 + p2 + __popcll(bk & lt)] = (int16_t)t;
+        p1 += __popcll(bl);
+        p2 += __popcll(bk);
+        p1_plain += __popcll(__ballot(low && !masked(t)));
+      }
+      if (lane == 0) {
+        n_list = n1;
+        n_list_plain = p1_plain;
+        n_list_hi = nk;
+      }
+    }
+    __syncthreads();
+    ntiles = n_list;
+    n_plain = n_list_plain;
+    n_hi = n_list_hi;
+  } else if constexpr (SPARSE) {
     if (wave == 0) {
       const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
@@ -331,10 +394,6 @@ void attn_fwd_kernel(FwdArgs a) {
   // is not a multiple of the wave count
   constexpr int KPW = (KPIECES + NW - 1) / NW;
   constexpr int VPW = (VPIECES + NW - 1) / NW;
-  // The K tile's scale rides along into the 256-byte tail of its buffer (all
-  // 64 lanes load the same word), so the softmax reads it from LDS: no
-  // scalar load, whose out-of-order return would make every LDS wait a full
-  // wait.
   auto load_k = [&](int t, int8_t* buf) {
     const int8_t* src = a.k_i8 + (kv_row0 + (size_t)t * kKT) * D;
 #pragma unroll
@@ -342,7 +401,6 @@ void attn_fwd_kernel(FwdArgs a) {
       const int piece = (wave + NW * j) % KPIECES;
       lds_dma16(src + k_src_off(piece), buf + piece * 1024);
     }
-    lds_dma4(kscale + t, buf + G::KBUF);
   };
   auto tile_kscale = [&](const int8_t* buf) {
     return *reinterpret_cast<const float*>(buf + G::KBUF);
@@ -354,6 +412,61 @@ void attn_fwd_kernel(FwdArgs a) {
       const int piece = (wave + NW * j) % VPIECES;
       lds_dma16(src + v_src_off(piece), buf + piece * 1024);
     }
+  };
+  // Half hs of promoted tile t: its 32 rows of the 16-bit K, in the same
+  // number of 1 KB loads as an INT8 K tile.
+  auto k16_src_off = [&](int piece) -> uint32_t {
+    const int r = piece * (1024 / G::K16ROW) + lane / G::K16SLOTS;
+    return (uint32_t)(r * G::K16ROW + (((lane % G::K16SLOTS) ^ G::k16swz(r)) * 16));
+  };
+  auto load_k16 = [&](int t, int hs, int8_t* buf) {
+    const int8_t* src = reinterpret_cast<const int8_t*>(a.k16 + (kv_row0 + (size_t)t * kKT + 32 * hs) * D);
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int piece = (wave + NW * j) % KPIECES;
+      lds_dma16(src + k16_src_off(piece), buf + piece * 1024);
+    }
+  };
+  // Step vt of the whole sequence: INT8 tiles [0, ntiles), then (promoted
+  // path) the two halves of each promoted tile. Steps past the end are
+  // clamped to the last one, and an empty sequence (a kept list with no
+  // usable entry) loads tile 0: such loads land in buffers nobody reads.
+  const int nsteps = ntiles + 2 * n_hi;
+  auto load_desc = [&](int vt, int& t, int& hs) {
+    vt = min(vt, nsteps - 1);
+    if (vt < 0) {
+      t = 0;
+      hs = -1;
+      return;
+    }
+    if constexpr (PROMOTE) {
+      if (vt < ntiles) {
+        t = tile_list[vt];
+        hs = -1;
+      } else {
+        const int u = vt - ntiles;
+        t = tile_list[ntiles + (u >> 1)];
+        hs = u & 1;
+      }
+    } else {
+      t = tile_of(vt);
+      hs = -1;
+    }
+  };
+  // The K tile's scale rides along into the 256-byte tail of its buffer (all
+  // 64 lanes load the same word), so the softmax reads it from LDS: no
+  // scalar load, whose out-of-order return would make every LDS wait a full
+  // wait. (A promoted half loads it too, unused, so that every step issues
+  // the same number of loads.)
+  auto issue = [&](int t, int hs, int8_t* kb, int8_t* vb) {
+    if constexpr (PROMOTE) {
+      if (hs >= 0) load_k16(t, hs, kb);
+      else load_k(t, kb);
+    } else {
+      load_k(t, kb);
+    }
+    lds_dma4(kscale + t, kb + G::KBUF);
+    load_v(t, vb);
   };
   // Waits go through the s_waitcnt builtin (not inline asm) so that the
   // compiler's own wait insertion knows which loads have already landed and
@@ -556,6 +669,110 @@ void attn_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ---- promoted halves (32 keys of a promoted tile, 16-bit Q K^T) -----------------
+  // S^T = K16 . Q16^T on v_mfma_f32_32x32x16_{bf16,f16}: lane (l32, h) holds
+  // channels 16*ks + 8*h + [0, 8) of K row l32 (A) and of its query row (B),
+  // the same lane layout as the INT8 product with 16-deep k-steps, so the fp32
+  // result has the S^T layout the softmax and P V already use.
+  int k16_frag_off[PROMOTE ? G::KS16 : 1];
+  if constexpr (PROMOTE) {
+#pragma unroll
+    for (int ks = 0; ks < G::KS16; ++ks)
+      k16_frag_off[ks] = l32 * G::K16ROW + (((2 * ks + h) ^ G::k16swz(l32)) * 16);
+  }
+  auto qk16 = [&](const int8_t* kb, const op_t (&qf16)[G::KS16], v16f& s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < G::KS16; ++ks) {
+      const op_t kf = *reinterpret_cast<const op_t*>(kb + k16_frag_off[ks]);
+      if (ks == 0) {
+        v16f z;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) z[r] = 0.0f;
+        s = MM::mma(kf, qf16[0], z);
+      } else {
+        s = MM::mma(kf, qf16[ks], s);
+      }
+    }
+  };
+  // Online softmax over a half: the logit of element r is c*S - cq, cq =
+  // fl32(c * (q . k_mean)) (the smoothing's per-row constant, which puts these
+  // logits in the INT8 path's frame), so the exponent is fma(c, S, -(cq + m)).
+  // Same reference rule, filter and rescale as the INT8 softmax; element r
+  // holds key key0 + 8*(r/4) + 4*h + r%4 and P goes out as the two 16-key
+  // groups of this 32-key block.
+  auto softmax_hi = [&](const v16f& s, int key0, float cq, op_t (&pf)[2]) __attribute__((always_inline)) {
+    const int lim = (row0 + l32) - (key0 + 4 * h);
+    auto exps = [&](float m) -> float {
+      const float cm = cq + m;
+      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        op_t pk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * hf + e;
+          const int off = 8 * (r >> 2) + (r & 3);
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(a.c, s[r], -cm));
+          if constexpr (CAUSAL) pe = off > lim ? 0.0f : pe;
+          lsum[e & 3] += pe;
+          pk[e] = (el_t)pe;
+        }
+        pf[hf] = pk;
+      }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    float psum = exps(m_ref[0]);
+    if (__ballot(psum > kSumFilter) != 0) {
+      float mxs = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        mxs = __builtin_fmaxf(mxs, (CAUSAL && off > lim) ? -__builtin_inff() : s[r]);
+      }
+      {
+        const int mi = __builtin_bit_cast(int, mxs);
+        const auto sw = __builtin_amdgcn_permlane32_swap(mi, mi, false, false);
+        mxs = __builtin_fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+      }
+      // c > 0: the max logit is the logit of the max product (-inf when the
+      // row sees no key of this half)
+      const float mx = __builtin_fmaf(a.c, mxs, -cq);
+      const float m_old = m_ref[0];
+      const float mc = __builtin_fmaxf(m_old, mx);
+      const bool move = mc > m_old + kTau;
+      if (__ballot(move) != 0) {
+        const float corr =
+            move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
+        m_ref[0] = move ? mc : m_old;
+        psum = exps(m_ref[0]);
+        l_run[0] *= corr;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][0][r] *= corr;
+      }
+    }
+    l_run[0] += psum;
+  };
+  // P V of a half: the two 16-key groups of 32-key block hs of the staged V
+  // tile (hs dispatched to compile-time offsets: with a runtime offset the
+  // compiler cannot tell the reads from the loads landing in other buffers
+  // and waits for all of them)
+  auto pv_hi = [&](const int8_t* vb, int hs, const op_t (&pf)[2]) __attribute__((always_inline)) {
+    static_for<0, 2>([&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      if (hs == H) {
+        op_t va[G::DB], vc[G::DB];
+        load_vgrp(vb, 2 * H, va);
+        load_vgrp(vb, 2 * H + 1, vc);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db][0] = MM::mma(va[db], pf[0], acc[db][0]);
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) acc[db][0] = MM::mma(vc[db], pf[1], acc[db][0]);
+      }
+    });
+  };
+
   // ---- pipeline ---------------------------------------------------------------------
   // Tile j's K (with its scale) and V live in buffer j % NBUF. Iteration it
   // issues the loads of tile it+PD into buffer (it+PD) % NBUF, whose last
@@ -578,9 +795,9 @@ void attn_fwd_kernel(FwdArgs a) {
   // prefetch distance (tiles) and the furthest tile the next iteration reads
   constexpr int PD = kLAG ? NBUF - 2 : NBUF - 1;
   static_for<0, PD>([&](auto j) {
-    const int tt = tile_of(min((int)j, ntiles - 1));
-    load_k(tt, kbuf(j));
-    load_v(tt, vbuf(j));
+    int tt, hs;
+    load_desc((int)j, tt, hs);
+    issue(tt, hs, kbuf(j), vbuf(j));
   });
   // lagged: the first iteration's "previous" V buffer gets tile 0's V too, so
   // that its zero P meets finite values (and the buffer is named at compile
@@ -611,7 +828,8 @@ void attn_fwd_kernel(FwdArgs a) {
     const std::integral_constant<int, J % NBUF> cur{};
     const std::integral_constant<int, (J + PD) % NBUF> nxt{};
     const std::integral_constant<int, (J + NBUF - 1) % NBUF> prv{};
-    const int tl = tile_of(min(it + PD, ntiles - 1));
+    int tl, tl_hs;
+    load_desc(it + PD, tl, tl_hs);
     // Every wave issues the loads at the same place, live or not, after the
     // reads of the current K tile: a separate branch for waves without rows
     // would merge its freshly issued loads into the live path's wait state.
@@ -632,8 +850,7 @@ void attn_fwd_kernel(FwdArgs a) {
         static_for<0, NVS>([&](auto gc) { load_vgrp(vp, decltype(gc)::value, vset[decltype(gc)::value]); });
         qk(kbuf(cur), s);
       }
-      load_k(tl, kbuf(nxt));
-      load_v(tl, vbuf(nxt));
+      issue(tl, tl_hs, kbuf(nxt), vbuf(nxt));
       if (wave_live) {
         auto lagged_pv = [&](auto qbc, auto gc) {
           constexpr int qb = decltype(qbc)::value;
@@ -651,8 +868,7 @@ void attn_fwd_kernel(FwdArgs a) {
         alpha = alpha_q * tile_kscale(kbuf(cur));
         qk(kbuf(cur), s);
       }
-      load_k(tl, kbuf(nxt));
-      load_v(tl, vbuf(nxt));
+      issue(tl, tl_hs, kbuf(nxt), vbuf(nxt));
       if (wave_live) {
         op_t p[2][QB][2];
         softmax(masked_c, s, alpha, t, p, [](auto, auto) {});
@@ -678,6 +894,68 @@ void attn_fwd_kernel(FwdArgs a) {
     static_for<0, NBUF>([&](auto j) {
       if (it % NBUF == (int)j) step(j, it, kYes);
     });
+  }
+  // promoted path: the halves of the promoted tiles, after the INT8 tiles
+  // (whose last steps have already prefetched the first halves)
+  if constexpr (PROMOTE) {
+    if (n_hi > 0) {
+      // the wave's 16-bit query row fragments and q . k_mean (fp32; the two
+      // lane halves hold the two halves of the row's channels)
+      op_t qf16[G::KS16];
+      const uint16_t* qg = a.q16 + (bhq * a.N + row0 + l32) * D;
+      const float* mean = a.k_mean + (size_t)kvu * D;
+      float part = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < G::KS16; ++ks) {
+        qf16[ks] = *reinterpret_cast<const op_t*>(qg + 16 * ks + 8 * h);
+        const float4 m0 = *reinterpret_cast<const float4*>(mean + 16 * ks + 8 * h);
+        const float4 m1 = *reinterpret_cast<const float4*>(mean + 16 * ks + 8 * h + 4);
+        const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)qf16[ks][e], mv[e], part);
+      }
+      const float cq = a.c * (part + __shfl_xor(part, 32, 64));
+      auto step_hi = [&](auto jc, int it) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        const std::integral_constant<int, J % NBUF> cur{};
+        const std::integral_constant<int, (J + PD) % NBUF> nxt{};
+        // the step PD ahead is a promoted half too (clamped to the last)
+        const int ul = min(it + PD, nsteps - 1) - ntiles;
+        const int tl = tile_list[ntiles + (ul >> 1)];
+        const int u = it - ntiles;
+        const int t = tile_list[ntiles + (u >> 1)];
+        const int hs = u & 1;
+        v16f s;
+        qk16(kbuf(cur), qf16, s);
+        load_k16(tl, ul & 1, kbuf(nxt));
+        lds_dma4(kscale + tl, kbuf(nxt) + G::KBUF);
+        load_v(tl, vbuf(nxt));
+        op_t p[2];
+        softmax_hi(s, t * kKT + 32 * hs, cq, p);
+        pv_hi(vbuf(cur), hs, p);
+        __builtin_amdgcn_s_waitcnt(vmcnt((PD - 1) * kLoadsPerIt));
+        barrier();
+      };
+      // unrolled NBUF times from the stage the first half lands in, so that
+      // consecutive steps name their buffers at compile time (a dispatch per
+      // step would merge the wait states of all buffers at the loop head)
+      auto hi_group = [&](auto j0c) __attribute__((always_inline)) {
+        constexpr int J0 = decltype(j0c)::value;
+        for (int base = ntiles; base + NBUF <= nsteps; base += NBUF) {
+          static_for<0, NBUF>([&](auto j) {
+            step_hi(std::integral_constant<int, (J0 + decltype(j)::value) % NBUF>{}, base + (int)j);
+          });
+        }
+      };
+      static_for<0, NBUF>([&](auto j0) {
+        if (ntiles % NBUF == (int)j0) hi_group(j0);
+      });
+      for (int it = nsteps - (nsteps - ntiles) % NBUF; it < nsteps; ++it) {
+        static_for<0, NBUF>([&](auto j) {
+          if (it % NBUF == (int)j) step_hi(j, it);
+        });
+      }
+    }
   }
   // no load may still be landing in LDS when the workgroup ends
   wait_all();
@@ -746,14 +1024,19 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
   static_assert(NW_DENSE % 4 == 0, "whole waves per SIMD");
   if (sparse) {
     const dim3 grid(a.B * a.Hq * a.nqb);
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3>), grid,
-                       dim3(NW_SPARSE * 64), 0, stream, a);
+    if (a.q16 != nullptr) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, true>), grid, dim3(4 * 64),
+                         0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3, false>), grid,
+                         dim3(NW_SPARSE * 64), 0, stream, a);
+    }
   } else {
     const int rows_wg = 32 * QBD * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
     constexpr int NBUF_DENSE = NW_DENSE * QBD >= 8 ? 4 : 3;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE>),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE, false>),
                        grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();
@@ -771,7 +1054,8 @@ int fwd_max_sparse_tiles() { return kMaxSparseTiles; }
 
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
-                           const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep, void* o,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
+                           const void* q16, const void* k16, const float* k_mean, void* o,
                            float* lse, hipStream_t stream) {
   FwdArgs a;
   a.q_i8 = q_i8;
@@ -783,6 +1067,9 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
   a.lse = lse;
   a.kv_idx = kv_idx;
   a.kv_cnt = kv_cnt;
+  a.q16 = static_cast<const uint16_t*>(q16);
+  a.k16 = static_cast<const uint16_t*>(k16);
+  a.k_mean = k_mean;
   a.B = s.B;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;

@@ -39,12 +39,16 @@ hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k
                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
                              int32_t* kv_cnt, void* workspace, hipStream_t stream);
 
-// Longest kept list qattn_fwd accepts (entries per query block).
+// Longest kept list qattn_fwd accepts (entries per query block); also the
+// most 64-key blocks (N / 64) the promoted path supports.
 int fwd_max_sparse_tiles();
 
+// Dense (kv_idx NULL), sparse (kv_idx set, q16 NULL) or promoted (kv_idx,
+// q16, k16 and k_mean set) attention forward.
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
-                           void* o, float* lse, hipStream_t stream);
+                           const void* q16, const void* k16, const float* k_mean, void* o,
+                           float* lse, hipStream_t stream);
 
 }  // namespace qattn

@@ -12,7 +12,9 @@
  *      first block, the diagonal blocks and the top fraction of the rest;
  *   3. compute S = Q K^T on INT8 matrix cores, an online base-2 softmax, and
  *      P V on FP16/BF16 matrix cores with FP32 accumulation, visiting only the
- *      kept key blocks when a mask is given.
+ *      kept key blocks when a mask is given -- or, promoting instead of
+ *      skipping, computing the kept blocks' Q K^T on 16-bit matrix cores and
+ *      every other block through the INT8 path.
  *
  * Conventions shared by every entry point:
  *   - Layouts are contiguous row-major: Q and O are [B, Hq, N, d]; K and V are
@@ -190,6 +192,44 @@ qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const flo
                          const int8_t* k_i8, const float* k_scale, const void* v,
                          const int32_t* kv_idx, const int32_t* kv_cnt, int32_t max_keep,
                          void* o, float* lse, void* stream);
+
+/*
+ * qattn_fwd_promoted -- promote instead of skip: the kept blocks at 16-bit
+ * Q K^T, every other visible block through the INT8 path of qattn_fwd.
+ *
+ * The ThriftAttention summary (gist.science/ja/paper/2605.23081), technical
+ * summary, method: the top-k block pairs are computed in 16-bit precision,
+ * the remaining pairs at low precision, and both are merged by a
+ * FlashAttention-2 style online softmax; its implementation paragraph runs
+ * the low-precision blocks first and the promoted ones after. Here the low
+ * path is INT8 and the kept list (typically from qattn_block_mask) names the
+ * promoted blocks. Per (b, hq) and query block i of 128 rows:
+ *   promoted = the distinct kept-list entries (the first kv_cnt of them) that
+ *              are in [0, N/64) and causally visible; low = every other
+ *              visible 64-key block;
+ *   first the low blocks, ascending, exactly as qattn_fwd's dense path;
+ *   then each promoted block, ascending, as two 32-key halves, with
+ *     S16 = q . k over the caller's 16-bit Q and K rows (fp32 accumulation),
+ *     cq  = fl32(fl32(log2(e)/sqrt(d)) * (q . k_mean)) (fp32 accumulation),
+ *     s   = fl32(log2(e)/sqrt(d)) * S16 - cq,
+ *   which is the smoothed logit q . (k - k_mean) in the INT8 path's units,
+ *   taken through the same online-softmax step as an INT8 tile;
+ *   O and lse as in qattn_fwd.
+ * In:  q_i8, q_scale, k_i8, k_scale, k_mean as written by qattn_smooth_quant
+ *      for these q and k; q [B,Hq,N,d] and k [B,Hkv,N,d] in p->dtype (the
+ *      inputs of that call); v [B,Hkv,N,d]; kv_idx [B,Hq,N/128,max_keep] and
+ *      kv_cnt [B,Hq,N/128] int32 (entries outside the range or the causal
+ *      range, duplicates and counts above max_keep are ignored).
+ * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
+ * Errors: NULL for any missing pointer but lse; SHAPE/UNSUPPORTED, also
+ *      UNSUPPORTED when N > 131072; ALIGN; ARG when max_keep < 1 or
+ *      max_keep > 2048; DEVICE.
+ */
+qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
+                                  const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                  const void* q, const void* k, const float* k_mean,
+                                  const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
+                                  int32_t max_keep, void* o, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,12 +64,12 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def run_gpu(qa, p, t, sparse=None, pools=None, with_lse=True):
+def run_gpu(qa, p, t, sparse=None, pools=None, with_lse=True, promote=False):
     """The whole path on cuda:0 through the C ABI; returns (plan, o) on device."""
     dev = torch.device("cuda:0")
     q, k, v = (t[x].to(dev) for x in "qkv")
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
-                   sparse=sparse, with_lse=with_lse, pools=pools)
+                   sparse=sparse, with_lse=with_lse, pools=pools, promote=promote)
     o = torch.empty_like(q)
     plan.run(q, k, v, o)
     torch.cuda.synchronize()
@@ -84,3 +84,19 @@ def head_slice(t, p, b: int, hqs):
            "k": t["k"][b:b + 1, hk:hk + 1].contiguous(),
            "v": t["v"][b:b + 1, hk:hk + 1].contiguous()}
     return sub, hk
+
+
+def same_lists(gi, gc, idx, cnt, ties):
+    """Per (b, hq, i): do the GPU's kept list (gi, gc) and the oracle's (idx,
+    cnt) agree? Asserts that they do wherever the oracle reports no near-tie,
+    and that the counts always agree; returns the agreement mask, so that the
+    attention outputs are compared only where both sides used the same list."""
+    assert np.array_equal(gc, cnt)
+    agree = np.all(gi == idx, axis=-1)
+    assert np.all(agree | ties)
+    return agree
+
+
+def block_rows(mask_bh_i: np.ndarray) -> np.ndarray:
+    """[B, Hq, nqb] block mask -> [B, Hq, N] row mask (128 rows per block)."""
+    return np.repeat(mask_bh_i, 128, axis=-1)

@@ -84,7 +84,15 @@ def _fw(p, **over):
                         check=False)
 
 
-@pytest.mark.parametrize("call", [_sq, _bm, _fw])
+def _fp(p, **over):
+    args = dict(qi=A, qs=A, ki=A, kscl=A, q=A, k=A, km=A, v=A, idx=A, cnt=A, mk=8, o=A, lse=None)
+    args.update(over)
+    return qa.qattn_fwd_promoted(p, args["qi"], args["qs"], args["ki"], args["kscl"], args["q"],
+                                 args["k"], args["km"], args["v"], args["idx"], args["cnt"],
+                                 args["mk"], args["o"], args["lse"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp])
 def test_problem_validation(lib, call):
     assert call(_p(B=0)) == SHAPE
     assert call(_p(Hq=0)) == SHAPE
@@ -143,6 +151,18 @@ def test_fwd_arguments(lib):
     assert _fw(p, idx=A, cnt=A, mk=0) == ARG
 
 
+def test_fwd_promoted_arguments(lib):
+    p = _p()
+    names = ["qi", "qs", "ki", "kscl", "q", "k", "km", "v", "idx", "cnt", "o"]
+    for name in names:
+        assert _fp(p, **{name: None}) == NULL, name
+        assert _fp(p, **{name: A + 8}) == ALIGN, name
+    assert _fp(p, lse=A + 4) == ALIGN
+    assert _fp(p, mk=0) == ARG
+    assert _fp(p, mk=2049) == ARG
+    assert _fp(_p(N=131072 + 128)) == UNSUP
+
+
 def test_max_keep_and_workspace_sizes(lib):
     p = _p(N=32768, Hq=32, Hkv=8)
     assert qa.qattn_max_keep(p, 1, 10) == 55
@@ -156,8 +176,8 @@ def test_max_keep_and_workspace_sizes(lib):
 
 
 def test_binding_has_the_c_names():
-    for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_workspace_bytes",
-              "qattn_max_keep", "qattn_status_str", "qattn_version"]:
+    for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
+              "qattn_workspace_bytes", "qattn_max_keep", "qattn_status_str", "qattn_version"]:
         assert callable(getattr(qa, n))
 
 

@@ -16,7 +16,7 @@ import torch
 import oracle
 from synthetic import make_case, make_config
 from parity_util import (TOL_EMU, COS_MIN, KERNEL_TAU, log, out_err, max_abs_rel, cos, to_np,
-                         run_gpu, head_slice)
+                         run_gpu, head_slice, same_lists, block_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,16 +132,63 @@ def test_sparse_fwd_matches_emulation(gpu_lib):
                      k_offset_std=3.0, outliers=4, sparse=(1, 10))
     log("sparse fwd N=2048")
     plan, o = run_gpu(gpu_lib, p, t, sparse=(1, 10))
-    idx, cnt = to_np(plan.kv_idx).astype(np.int32), to_np(plan.kv_cnt).astype(np.int32)
-    sq = oracle.smooth_quant(t["q"], t["k"])
+    # each side uses its own mask; outputs are compared where the lists agree
+    sq = oracle.smooth_quant(t["q"], t["k"], pools=True)
+    idx, cnt, ties = oracle.block_mask(sq["q_pool"], sq["k_pool"], p.Hq, p.Hkv, True, 1, 10,
+                                       plan.max_keep)
+    rows = block_rows(same_lists(to_np(plan.kv_idx), to_np(plan.kv_cnt), idx, cnt, ties))
     O_emu, O_pre, _ = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                sq["k_scale"], t["v"], True, p.Hq, p.Hkv,
                                                kv_idx=idx, kv_cnt=cnt, tau=KERNEL_TAU)
     O_ex, _ = oracle.exact_attention(t["q"], t["k"], t["v"], True, idx, cnt)
     og = to_np(o)
-    e, c = out_err(og, O_pre, p.dtype), cos(og, O_ex)
-    log(f"  err_vs_emu={e:.3e} cos_exact_same_mask={c:.6f}")
+    e, c = out_err(og[rows], O_pre[rows], p.dtype), cos(og[rows], O_ex[rows])
+    log(f"  err_vs_emu={e:.3e} cos_exact_same_mask={c:.6f} rows={rows.mean():.3f}")
     assert e <= TOL_EMU and c >= COS_MIN
+
+
+def test_sparse_fwd_empty_and_invalid_lists(gpu_lib):
+    # kept lists with no usable entry (count 0, or only entries out of range or
+    # past the causal range) give O = 0 and lse = -inf; a list of duplicates of
+    # one block equals that block alone
+    p, t = make_case(B=1, Hq=2, Hkv=1, N=512, d=64, dtype="bf16", causal=True, seed=36)
+    log("sparse fwd, empty / invalid / duplicate kept lists")
+    dev = torch.device("cuda:0")
+    qa = gpu_lib
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev, with_lse=True)
+    plan.smooth_quant(q, k)
+    nqb, mk = p.N // 128, 4
+    idx = torch.full((1, 2, nqb, mk), -1, dtype=torch.int32)
+    cnt = torch.zeros((1, 2, nqb), dtype=torch.int32)
+    # head 0: count 0 everywhere; head 1, block i: entries -1, 8 (out of range),
+    # 2i + 2 (past the causal range when in range), count 3
+    for i in range(nqb):
+        idx[0, 1, i, :3] = torch.tensor([-1, 8, 2 * i + 2])
+        cnt[0, 1, i] = 3
+    o = torch.full_like(q, 7.0)
+    lse = torch.zeros((1, 2, p.N), dtype=torch.float32, device=dev)
+    qa.qattn_fwd(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
+                 idx.to(dev), cnt.to(dev), mk, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert torch.all(torch.isneginf(lse))
+    # duplicates of block 0 (visible to every row) = block 0 once
+    idx_dup = torch.zeros((1, 2, nqb, mk), dtype=torch.int32)
+    cnt_dup = torch.full((1, 2, nqb), mk, dtype=torch.int32)
+    idx_one = torch.zeros((1, 2, nqb, mk), dtype=torch.int32)
+    cnt_one = torch.ones((1, 2, nqb), dtype=torch.int32)
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    qa.qattn_fwd(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
+                 idx_one.to(dev), cnt_one.to(dev), mk, o1, None)
+    qa.qattn_fwd(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
+                 idx_dup.to(dev), cnt_dup.to(dev), mk, o2, None)
+    torch.cuda.synchronize()
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    _, O_pre, _ = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"],
+                                           t["v"], True, 2, 1, kv_idx=idx_one.numpy(),
+                                           kv_cnt=cnt_one.numpy(), tau=KERNEL_TAU)
+    assert out_err(to_np(o1), O_pre, p.dtype) <= TOL_EMU
 
 
 def test_keep_all_mask_equals_dense_bit_exact(gpu_lib):
@@ -219,10 +266,11 @@ def _sampled_check(qa, c, n_blocks=3):
                                            sparse[0], sparse[1], plan.max_keep)
         gi = to_np(plan.kv_idx)[b, hqs]
         gc = to_np(plan.kv_cnt)[b, hqs]
-        ok = ~ties[0]
-        assert np.array_equal(gc, cnt[0])
-        assert np.array_equal(gi[ok], idx[0][ok])
-        kv_idx, kv_cnt = gi[None].astype(np.int32), gc[None].astype(np.int32)
+        agree = same_lists(gi[None], gc[None], idx, cnt, ties)
+        # compare only the sampled blocks whose lists agree (all but near-ties)
+        sel = [(0, n, i) for (_, n, i) in sel if agree[0, n, i]]
+        blocks = sorted({i for (_, _, i) in sel})
+        kv_idx, kv_cnt = idx, cnt
     O_emu, O_pre, _ = oracle.emulate_attention(ref["q_i8"], ref["q_scale"], ref["k_i8"],
                                                ref["k_scale"], sub["v"], p.causal, ps.Hq, 1,
                                                kv_idx=kv_idx, kv_cnt=kv_cnt, blocks=sel,
