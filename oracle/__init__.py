@@ -19,6 +19,9 @@ written for reading, not for speed:
 * ``emulate_promoted_attention`` / ``promote_plan`` -- promote instead of
   skip: the kept blocks at 16-bit Q K^T, every other visible block through
   the INT8 path, merged by the same online softmax.
+* ``head_error`` / ``adaptive_lists`` -- adaptive per-head precision: a
+  sampled RMS logit error of the INT8 path per head, and the kept lists that
+  run the heads above a threshold entirely at 16-bit Q K^T.
 
 Sources (the explainer pages these follow):
 
@@ -44,4 +47,5 @@ from .quant import (k_channel_mean, quantize_block, smooth_quant,  # noqa: F401
                     pool_vector_quant)
 from .mask import block_mask, max_keep, select_blocks  # noqa: F401
 from .attention import (exact_attention, emulate_attention, emulate_promoted_attention,  # noqa: F401
-                        promote_plan, softmax_scale_log2)
+                        promote_plan, softmax_scale_log2, head_error, head_error_sample,
+                        adaptive_lists)

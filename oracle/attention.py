@@ -313,3 +313,78 @@ def emulate_promoted_attention(q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, ca
         O_pre[b, hq, r0:r0 + Q_BLOCK] = o32
         O[b, hq, r0:r0 + Q_BLOCK] = round_to_dtype(o32, out_dtype)
     return O, O_pre, lse
+
+
+def head_error_sample(N: int):
+    """The (query row, key) sample of ``head_error``.
+
+    Up to 64 query rows, one from each of as many evenly spaced query blocks
+    (block i_u = floor(u * nqb / nsq), row 128*i_u + (37*u + 11) mod 128), and
+    up to 256 keys, one from each of as many evenly spaced key blocks (block
+    j_w = floor(w * nkb / nsk), key 64*j_w + (29*w + 5) mod 64). Every
+    (row, key) combination is a sampled pair, causally visible or not: the
+    statistic is about the quantization of the logits, not the mask.
+    """
+    nqb, nkb = N // Q_BLOCK, N // K_BLOCK
+    nsq, nsk = min(nqb, 64), min(nkb, 256)
+    rows = np.array([Q_BLOCK * ((u * nqb) // nsq) + (37 * u + 11) % Q_BLOCK for u in range(nsq)])
+    keys = np.array([K_BLOCK * ((w * nkb) // nsk) + (29 * w + 5) % K_BLOCK for w in range(nsk)])
+    return rows, keys
+
+
+def head_error(q_i8, q_scale, k_i8, k_scale, q, k, k_mean, Hq: int, Hkv: int):
+    """Data-free per-head error proxy of the INT8 Q K^T (adaptive precision).
+
+    The SageAttention explainer (aibr.jp/archives/102657), sections 1-4, names
+    adaptive quantization as its third ingredient: the quantization is set per
+    layer or head so that the heads that need it keep more precision, and the
+    adaptive version is faster at no loss. The page gives no rule. Here the
+    rule uses only the head's own Q and K: over the pairs of
+    ``head_error_sample``,
+      s8  = fl32(S * alpha), S the exact INT8 code product and alpha as in
+            ``emulate_attention`` (the INT8 path's base-2 logit);
+      s16 = c * (q . k - q . k_mean), c = fl32(log2(e)/sqrt(d)) (the 16-bit
+            path's logit, exact here);
+      err = sqrt(mean over the pairs of (s8 - s16)^2), in log2 units,
+    i.e. the RMS logit error the INT8 path adds in that head (a P is off by a
+    factor 2^(s8 - s16)). Returns err [B, Hq] fp64.
+    """
+    q64, k64 = _as_f64(q), _as_f64(k)
+    mean64 = np.asarray(k_mean, dtype=np.float32).astype(np.float64)
+    B, _, N, d = q_i8.shape
+    group = Hq // Hkv
+    c = softmax_scale_log2(d)
+    rows, keys = head_error_sample(N)
+    err = np.zeros((B, Hq))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // group
+            S = q_i8[b, hq, rows].astype(np.float64) @ k_i8[b, hk, keys].astype(np.float64).T
+            alpha_q = (np.asarray(q_scale[b, hq, rows // Q_BLOCK], dtype=np.float32) * c
+                       ).astype(np.float32)
+            alpha = (alpha_q[:, None] * np.asarray(k_scale[b, hk, keys // K_BLOCK],
+                                                   dtype=np.float32)[None, :]).astype(np.float32)
+            s8 = (S.astype(np.float32) * alpha).astype(np.float64)
+            qr = q64[b, hq, rows]
+            s16 = float(c) * (qr @ k64[b, hk, keys].T - (qr @ mean64[b, hk])[:, None])
+            err[b, hq] = math.sqrt(np.mean((s8 - s16) ** 2))
+    return err
+
+
+def adaptive_lists(head_hi, N: int, causal: bool):
+    """Kept lists that promote every visible block of the flagged heads and
+    none of the others (head_hi [B, Hq] bool): the adaptive forward is the
+    promoted forward with these lists."""
+    B, Hq = head_hi.shape
+    nqb, nkb = N // Q_BLOCK, N // K_BLOCK
+    idx = np.full((B, Hq, nqb, nkb), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hq, nqb), dtype=np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            if not head_hi[b, h]:
+                continue
+            for i in range(nqb):
+                vis = _kv_tiles_dense(i, N, causal, K_BLOCK)
+                idx[b, h, i, :len(vis)] = vis
+                cnt[b, h, i] = len(vis)
+    return idx, cnt
