@@ -77,6 +77,10 @@ def load(path: str = LIB_PATH):
     lib.qattn_fwd.restype = ctypes.c_int
     lib.qattn_fwd_promoted.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.qattn_fwd_promoted.restype = ctypes.c_int
+    lib.qattn_head_error.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.qattn_head_error.restype = ctypes.c_int
+    lib.qattn_fwd_adaptive.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.qattn_fwd_adaptive.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -187,6 +191,26 @@ def qattn_fwd_promoted(p, q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, kv_idx,
                                    _stream(stream))
     if check:
         _check(st, "qattn_fwd_promoted")
+    return st
+
+
+def qattn_head_error(p, q_i8, q_scale, k_i8, k_scale, q, k, k_mean, threshold, head_err,
+                     head_hi=None, stream=None, check=True) -> int:
+    st = load().qattn_head_error(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_i8),
+                                 _ptr(k_scale), _ptr(q), _ptr(k), _ptr(k_mean), float(threshold),
+                                 _ptr(head_err), _ptr(head_hi), _stream(stream))
+    if check:
+        _check(st, "qattn_head_error")
+    return st
+
+
+def qattn_fwd_adaptive(p, q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, head_hi, o, lse=None,
+                       stream=None, check=True) -> int:
+    st = load().qattn_fwd_adaptive(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_i8),
+                                   _ptr(k_scale), _ptr(q), _ptr(k), _ptr(k_mean), _ptr(v),
+                                   _ptr(head_hi), _ptr(o), _ptr(lse), _stream(stream))
+    if check:
+        _check(st, "qattn_fwd_adaptive")
     return st
 
 

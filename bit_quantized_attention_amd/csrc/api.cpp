@@ -139,7 +139,7 @@ qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const flo
   if (kv_idx != nullptr && (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()))
     return QATTN_ERR_ARG;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
-                                         max_keep, nullptr, nullptr, nullptr, o, lse,
+                                         max_keep, nullptr, nullptr, nullptr, nullptr, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -160,7 +160,45 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
     if (x && misaligned(x)) return QATTN_ERR_ALIGN;
   if (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()) return QATTN_ERR_ARG;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
-                                         max_keep, q, k, k_mean, o, lse,
+                                         max_keep, q, k, k_mean, nullptr, o, lse,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_head_error(const qattn_problem_t* p, const int8_t* q_i8,
+                                const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                const void* q, const void* k, const float* k_mean,
+                                float threshold, float* head_err, int32_t* head_hi,
+                                void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !q || !k || !k_mean || !head_err)
+    return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_i8, q_scale, k_i8, k_scale, q, k, k_mean, head_err, head_hi};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (!(threshold >= 0.0f) || !std::isfinite(threshold)) return QATTN_ERR_ARG;
+  return launched(qattn::launch_head_error(s, q_i8, q_scale, k_i8, k_scale, q, k, k_mean,
+                                           threshold, head_err, head_hi,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_fwd_adaptive(const qattn_problem_t* p, const int8_t* q_i8,
+                                  const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                  const void* q, const void* k, const float* k_mean,
+                                  const void* v, const int32_t* head_hi, void* o, float* lse,
+                                  void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.nkb() > qattn::fwd_max_sparse_tiles()) return QATTN_ERR_UNSUPPORTED;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !q || !k || !k_mean || !v || !head_hi || !o)
+    return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, head_hi, o, lse};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, nullptr, nullptr, 0,
+                                         q, k, k_mean, head_hi, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 

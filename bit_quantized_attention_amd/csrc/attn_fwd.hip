@@ -118,10 +118,13 @@ struct FwdArgs {
   float* lse;
   const int32_t* kv_idx;
   const int32_t* kv_cnt;
-  // promoted path: the 16-bit Q and K and the K smoothing mean
+  // promoted path: the 16-bit Q and K and the K smoothing mean; head_hi
+  // (adaptive precision) promotes every visible block of the flagged heads
+  // and none of the others, in place of a kept list
   const uint16_t* q16;
   const uint16_t* k16;
   const float* k_mean;
+  const int32_t* head_hi;
   int B, Hq, Hkv, N, group, g4, nqb, nkb, max_keep;
   float c;  // fl32(log2(e) / sqrt(d))
 };
@@ -274,9 +277,10 @@ void attn_fwd_kernel(FwdArgs a) {
     // tile_list[n1, n1 + n_hi).
     const int nvis = CAUSAL ? min(a.nkb, wg_last_row / kKT + 1) : a.nkb;
     const int nwords = (nvis + 31) >> 5;
-    for (int w = threadIdx.x; w < nwords; w += NW * 64) kept_bits[w] = 0u;
+    const uint32_t fill = (a.head_hi != nullptr && a.head_hi[bhq] != 0) ? ~0u : 0u;
+    for (int w = threadIdx.x; w < nwords; w += NW * 64) kept_bits[w] = fill;
     __syncthreads();
-    {
+    if (a.head_hi == nullptr) {
       const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
       for (int e = threadIdx.x; e < cnt; e += NW * 64) {
@@ -1055,8 +1059,8 @@ int fwd_max_sparse_tiles() { return kMaxSparseTiles; }
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
-                           const void* q16, const void* k16, const float* k_mean, void* o,
-                           float* lse, hipStream_t stream) {
+                           const void* q16, const void* k16, const float* k_mean,
+                           const int32_t* head_hi, void* o, float* lse, hipStream_t stream) {
   FwdArgs a;
   a.q_i8 = q_i8;
   a.q_scale = q_scale;
@@ -1070,6 +1074,7 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
   a.q16 = static_cast<const uint16_t*>(q16);
   a.k16 = static_cast<const uint16_t*>(k16);
   a.k_mean = k_mean;
+  a.head_hi = head_hi;
   a.B = s.B;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
@@ -1081,7 +1086,7 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
   a.max_keep = max_keep;
   // the softmax temperature folded with the change to base 2, rounded once
   a.c = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
-  const bool sparse = kv_idx != nullptr;
+  const bool sparse = kv_idx != nullptr || head_hi != nullptr;
   if (s.d == 128)
     return s.bf16 ? launch_d<128, true>(a, s.causal, sparse, stream)
                   : launch_d<128, false>(a, s.causal, sparse, stream);

@@ -43,12 +43,20 @@ hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k
 // most 64-key blocks (N / 64) the promoted path supports.
 int fwd_max_sparse_tiles();
 
-// Dense (kv_idx NULL), sparse (kv_idx set, q16 NULL) or promoted (kv_idx,
-// q16, k16 and k_mean set) attention forward.
+// Dense (kv_idx NULL), sparse (kv_idx set, q16 NULL), promoted (kv_idx, q16,
+// k16 and k_mean set) or adaptive (head_hi, q16, k16 and k_mean set, kv_idx
+// NULL) attention forward.
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
-                           const void* q16, const void* k16, const float* k_mean, void* o,
-                           float* lse, hipStream_t stream);
+                           const void* q16, const void* k16, const float* k_mean,
+                           const int32_t* head_hi, void* o, float* lse, hipStream_t stream);
+
+// Per-head sampled RMS logit error of the INT8 path against the 16-bit path;
+// head_hi (optional) gets err > threshold.
+hipError_t launch_head_error(const Shape& s, const int8_t* q_i8, const float* q_scale,
+                             const int8_t* k_i8, const float* k_scale, const void* q,
+                             const void* k, const float* k_mean, float threshold,
+                             float* head_err, int32_t* head_hi, hipStream_t stream);
 
 }  // namespace qattn

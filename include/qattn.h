@@ -231,6 +231,57 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
                                   const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                                   int32_t max_keep, void* o, float* lse, void* stream);
 
+/*
+ * qattn_head_error -- per-head error proxy of the INT8 Q K^T (adaptive
+ * per-head precision, data-free).
+ *
+ * The SageAttention explainer (aibr.jp/archives/102657), sections 1-4, names
+ * adaptive quantization, set per layer or head so that the parts that need it
+ * keep more precision, as the method's third ingredient; it gives no rule.
+ * This library measures, per (b, hq), over a fixed sample of up to 64 query
+ * rows (row 128*floor(u*nqb/nsq) + (37u+11) mod 128, u < nsq = min(nqb, 64))
+ * and up to 256 keys (key 64*floor(w*nkb/nsk) + (29w+5) mod 64,
+ * w < nsk = min(nkb, 256)), all pairs, visible or not:
+ *   s8  = fl32(S * alpha): S the exact INT8 code product, alpha as in
+ *         qattn_fwd (the INT8 path's base-2 logit);
+ *   s16 = c * (q . k - q . k_mean), c = fl32(log2(e)/sqrt(d)), on the 16-bit
+ *         Q and K with fp32 accumulation (the 16-bit path's logit);
+ *   head_err = sqrt(mean (s8 - s16)^2) (fp32, fixed summation order);
+ *   head_hi  = head_err > threshold ? 1 : 0.
+ * In:  q_i8, q_scale, k_i8, k_scale, k_mean from qattn_smooth_quant of q, k
+ *      (the 16-bit inputs, p->dtype).
+ * Out: head_err [B,Hq] f32; head_hi [B,Hq] int32 or NULL.
+ * Errors: NULL (head_hi may be NULL); SHAPE/UNSUPPORTED; ALIGN; ARG when the
+ *      threshold is negative or not finite; DEVICE.
+ */
+qattn_status_t qattn_head_error(const qattn_problem_t* p, const int8_t* q_i8,
+                                const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                const void* q, const void* k, const float* k_mean,
+                                float threshold, float* head_err, int32_t* head_hi,
+                                void* stream);
+
+/*
+ * qattn_fwd_adaptive -- attention with the precision of Q K^T chosen per
+ * head: every visible block of a head with head_hi[b,hq] != 0 at 16-bit
+ * Q K^T, every block of the other heads through the INT8 path.
+ *
+ * Same computation as qattn_fwd_promoted with a kept list holding all visible
+ * blocks for the flagged heads and none for the others (same source
+ * passages, plus the SageAttention explainer's adaptive quantization, sections
+ * 1-4). A flagged head's tiles run as 32-key halves in ascending order; an
+ * unflagged head's as 64-key INT8 tiles in ascending order.
+ * In:  as qattn_fwd_promoted; head_hi [B,Hq] int32 (e.g. from
+ *      qattn_head_error).
+ * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
+ * Errors: NULL for any missing pointer but lse; SHAPE/UNSUPPORTED, also
+ *      UNSUPPORTED when N > 131072; ALIGN; DEVICE.
+ */
+qattn_status_t qattn_fwd_adaptive(const qattn_problem_t* p, const int8_t* q_i8,
+                                  const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                  const void* q, const void* k, const float* k_mean,
+                                  const void* v, const int32_t* head_hi, void* o, float* lse,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,7 +92,23 @@ def _fp(p, **over):
                                  args["mk"], args["o"], args["lse"], stream=0, check=False)
 
 
-@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp])
+def _he(p, **over):
+    args = dict(qi=A, qs=A, ki=A, kscl=A, q=A, k=A, km=A, thr=0.02, err=A, hi=None)
+    args.update(over)
+    return qa.qattn_head_error(p, args["qi"], args["qs"], args["ki"], args["kscl"], args["q"],
+                               args["k"], args["km"], args["thr"], args["err"], args["hi"],
+                               stream=0, check=False)
+
+
+def _fa(p, **over):
+    args = dict(qi=A, qs=A, ki=A, kscl=A, q=A, k=A, km=A, v=A, hi=A, o=A, lse=None)
+    args.update(over)
+    return qa.qattn_fwd_adaptive(p, args["qi"], args["qs"], args["ki"], args["kscl"], args["q"],
+                                 args["k"], args["km"], args["v"], args["hi"], args["o"],
+                                 args["lse"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa])
 def test_problem_validation(lib, call):
     assert call(_p(B=0)) == SHAPE
     assert call(_p(Hq=0)) == SHAPE
@@ -163,6 +179,26 @@ def test_fwd_promoted_arguments(lib):
     assert _fp(_p(N=131072 + 128)) == UNSUP
 
 
+def test_head_error_arguments(lib):
+    p = _p()
+    for name in ["qi", "qs", "ki", "kscl", "q", "k", "km", "err"]:
+        assert _he(p, **{name: None}) == NULL, name
+        assert _he(p, **{name: A + 8}) == ALIGN, name
+    assert _he(p, hi=A + 4) == ALIGN
+    assert _he(p, thr=-1.0) == ARG
+    assert _he(p, thr=float("nan")) == ARG
+    assert _he(p, thr=float("inf")) == ARG
+
+
+def test_fwd_adaptive_arguments(lib):
+    p = _p()
+    for name in ["qi", "qs", "ki", "kscl", "q", "k", "km", "v", "hi", "o"]:
+        assert _fa(p, **{name: None}) == NULL, name
+        assert _fa(p, **{name: A + 8}) == ALIGN, name
+    assert _fa(p, lse=A + 4) == ALIGN
+    assert _fa(_p(N=131072 + 128)) == UNSUP
+
+
 def test_max_keep_and_workspace_sizes(lib):
     p = _p(N=32768, Hq=32, Hkv=8)
     assert qa.qattn_max_keep(p, 1, 10) == 55
@@ -177,7 +213,8 @@ def test_max_keep_and_workspace_sizes(lib):
 
 def test_binding_has_the_c_names():
     for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
-              "qattn_workspace_bytes", "qattn_max_keep", "qattn_status_str", "qattn_version"]:
+              "qattn_head_error", "qattn_fwd_adaptive", "qattn_workspace_bytes", "qattn_max_keep",
+              "qattn_status_str", "qattn_version"]:
         assert callable(getattr(qa, n))
 
 
