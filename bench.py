@@ -1,7 +1,7 @@
 """Benchmark of the quantized attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
-                    [--promote]
+                    [--promote | --adaptive TAU]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -23,6 +23,11 @@ mask keeps (the workload's keep ratio, else first + diagonal + top 10 %) run at
 algorithmic operations are those of the dense problem (4*d per visible pair),
 of which 2*d per promoted pair and 2*d per pair for P V are 16-bit; the peak
 is the matrix bound of that mix (INT8 and 16-bit work each at its own peak).
+
+With ``--adaptive TAU`` the step runs qattn_head_error after the smoothing
+(its per-head INT8 logit error on a fixed sample) and then qattn_fwd_adaptive:
+the heads whose error exceeds TAU take 16-bit Q K^T on every block, the rest
+INT8. Operations and peak are counted the same way.
 """
 
 from __future__ import annotations
@@ -113,6 +118,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--promote", action="store_true",
                     help="promote the kept blocks to 16-bit Q K^T instead of skipping the rest")
+    ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
+                    help="per-head precision: heads whose sampled INT8 logit error exceeds TAU "
+                         "(log2 units) run at 16-bit Q K^T")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -143,7 +151,7 @@ def sparse_pairs(kv_idx: np.ndarray, kv_cnt: np.ndarray, causal: bool) -> float:
     return float(total)
 
 
-def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False):
+def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -171,9 +179,13 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False):
             num, den = keep
             idx, cnt, _ = oracle.block_mask(sq["q_pool"], sq["k_pool"], len(hqs), 1, p.causal,
                                             num, den)
+        if adaptive is not None:
+            err = oracle.head_error(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], q, k,
+                                    sq["k_mean"], len(hqs), 1)
+            idx, cnt = oracle.adaptive_lists(err > adaptive, p.N, p.causal)
         for n in range(len(hqs)):
             blocks = [(0, n, i) for i in range(nqb)]
-            if promote:
+            if promote or adaptive is not None:
                 oracle.emulate_promoted_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                   sq["k_scale"], q, k, sq["k_mean"], v, p.causal,
                                                   len(hqs), 1, idx, cnt, blocks=blocks)
@@ -182,7 +194,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False):
                                          p.causal, len(hqs), 1, kv_idx=idx, kv_cnt=cnt,
                                          blocks=blocks)
             heads_done += 1
-            if sparse and not promote:
+            if sparse and not promote and adaptive is None:
                 done_ops += 4.0 * p.d * sparse_pairs(idx[:, n:n + 1], cnt[:, n:n + 1], p.causal)
             else:
                 pairs = p.N * (p.N + 1) / 2 if p.causal else float(p.N) ** 2
@@ -198,7 +210,8 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False):
         "cores": int(threads),
         "kind": "oracle",
         "sample": f"oracle smooth_quant + {'block_mask + ' if sparse else ''}"
-                  f"{'emulate_promoted_attention' if promote else 'emulate_attention'} "
+                  f"{'head_error + ' if adaptive is not None else ''}"
+                  f"{'emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention'} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
                   f"({el:.1f} s); numpy BLAS {blas}",
     }
@@ -222,14 +235,40 @@ def main():
     p, t = make_config(args.config)
     dev = torch.device("cuda:0")
     q, k, v = (t[x].to(dev) for x in "qkv")
-    keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
+    if args.promote and args.adaptive is not None:
+        raise SystemExit("--promote and --adaptive are exclusive")
+    adaptive = args.adaptive is not None
+    if adaptive:
+        keep = None
+    else:
+        keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
                    sparse=keep, promote=args.promote)
     o = torch.empty_like(q)
+    head_err = torch.empty((p.B, p.Hq), dtype=torch.float32, device=dev)
+    head_hi = torch.empty((p.B, p.Hq), dtype=torch.int32, device=dev)
+
+    def head_precision():
+        qa.qattn_head_error(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, q, k,
+                            plan.k_mean, args.adaptive, head_err, head_hi)
+
+    def attention():
+        if args.promote:
+            plan.fwd_promoted(q, k, v, o)
+        elif adaptive:
+            qa.qattn_fwd_adaptive(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, q,
+                                  k, plan.k_mean, v, head_hi, o, plan.lse)
+        else:
+            plan.fwd(v, o)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        plan.run(q, k, v, o)
+        plan.smooth_quant(q, k)
+        if keep is not None:
+            plan.block_mask()
+        if adaptive:
+            head_precision()
+        attention()
     torch.cuda.synchronize()
 
     # timed region: K whole steps; the attention kernel's own launches are
@@ -245,12 +284,11 @@ def main():
         plan.smooth_quant(q, k)
         if keep is not None:
             plan.block_mask()
+        if adaptive:
+            head_precision()
         sq_ev[s][1].record(stream)
         ev[s][0].record(stream)
-        if args.promote:
-            plan.fwd_promoted(q, k, v, o)
-        else:
-            plan.fwd(v, o)
+        attention()
         ev[s][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -278,16 +316,26 @@ def main():
     literal = 4.0 * p.N * p.N * p.d * p.Hq * p.B
     peak = PEAK_INT8_TOPS
     promote_info = None
-    if args.promote:
+    if args.promote or adaptive:
         # every visible pair: 2*d for Q K^T (INT8, or 16-bit when promoted) and
         # 2*d for P V (16-bit)
         alg = dense_algorithmic_ops(p)
-        prom = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
+        if adaptive:
+            prom = (alg / (4.0 * p.d)) * float(head_hi.float().mean().item())
+        else:
+            prom = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
         ops_16 = alg / 2 + 2.0 * p.d * prom
         ops_i8 = alg - ops_16
         peak = alg / (ops_i8 / PEAK_INT8_TOPS + ops_16 / PEAK_BF16_TFLOPS)
-        promote_info = {"keep": list(keep), "promoted_pair_fraction": prom / (alg / (4.0 * p.d)),
+        promote_info = {"keep": list(keep) if keep else None,
+                        "promoted_pair_fraction": prom / (alg / (4.0 * p.d)),
                         "ops_int8_per_launch": ops_i8, "ops_16bit_per_launch": ops_16}
+        if adaptive:
+            he = head_err.cpu().numpy()
+            promote_info.update({"threshold": args.adaptive, "heads_16bit": int(head_hi.sum()),
+                                 "heads": int(head_hi.numel()),
+                                 "head_error_min": float(he.min()),
+                                 "head_error_max": float(he.max())})
     elif p.sparse is not None:
         pairs = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
         alg = 4.0 * p.d * pairs
@@ -310,10 +358,12 @@ def main():
         "dtype": "i8+bf16" if p.dtype == "bf16" else "i8+f16",
         "data": "synthetic (seeded Gaussian Q/K/V with per-channel K offsets and outlier channels)",
         "config": {"workload": p.name + (" (kept blocks promoted to 16-bit QK^T, the rest INT8)"
-                                         if args.promote else ""),
+                                         if args.promote else "") +
+                   (f" (per-head precision, error threshold {args.adaptive})" if adaptive else ""),
                    "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
-                   "causal": p.causal, "sparse": None if args.promote else p.sparse,
-                   "promote": list(keep) if args.promote else None, "input_dtype": p.dtype},
+                   "causal": p.causal, "sparse": None if (args.promote or adaptive) else p.sparse,
+                   "promote": list(keep) if args.promote else None,
+                   "adaptive_threshold": args.adaptive, "input_dtype": p.dtype},
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
@@ -337,9 +387,10 @@ def main():
         "blended_mfma_peak_tops": 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS),
     }
     if promote_info is not None:
-        res["promote"] = promote_info
+        res["adaptive" if adaptive else "promote"] = promote_info
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote)
+        res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote,
+                                               args.adaptive)
     print(json.dumps(res))
 
 
