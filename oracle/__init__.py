@@ -19,6 +19,9 @@ written for reading, not for speed:
 * ``emulate_promoted_attention`` / ``promote_plan`` -- promote instead of
   skip: the kept blocks at 16-bit Q K^T, every other visible block through
   the INT8 path, merged by the same online softmax.
+* ``lowbit_block_mask`` (module ``lowbit``) -- the element-level 4-bit
+  block estimator: MX FP4 Q and smoothed K, the block score as the largest
+  estimated product over the block's visible pairs, the same selection rule.
 * ``head_error`` / ``adaptive_lists`` -- adaptive per-head precision: a
   sampled RMS logit error of the INT8 path per head, and the kept lists that
   run the heads above a threshold entirely at 16-bit Q K^T.
@@ -31,9 +34,10 @@ Sources (the explainer pages these follow):
 * ThriftAttention summary, gist.science/ja/paper/2605.23081, technical summary,
   method: block importance from the dot product of the block mean vectors,
   top-k block pairs, online softmax merge as in FlashAttention-2.
-* SALE explainer, aibr.jp/archives/118208, sections 1 and 3: a cheap low-bit
+* SALE explainer, aibr.jp/archives/118208, sections 1-3: a cheap low-bit
   estimate turned into a block-sparse plan that skips the rest, with the sink
-  (first) and local (diagonal) stripes kept.
+  (first) and local (diagonal) stripes kept; element-level 4-bit estimates of
+  the query-key products.
 
 Parity pins: every function here is pinned by CPU tests against closed forms,
 invariants, a library routine that computes the same definition, or brute force
@@ -49,3 +53,4 @@ from .mask import block_mask, max_keep, select_blocks  # noqa: F401
 from .attention import (exact_attention, emulate_attention, emulate_promoted_attention,  # noqa: F401
                         promote_plan, softmax_scale_log2, head_error, head_error_sample,
                         adaptive_lists)
+from .lowbit import lowbit_block_mask, lowbit_scores, mxfp4_quantize  # noqa: F401,E402
