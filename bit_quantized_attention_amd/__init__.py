@@ -77,6 +77,10 @@ def load(path: str = LIB_PATH):
     lib.qattn_fwd.restype = ctypes.c_int
     lib.qattn_fwd_promoted.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.qattn_fwd_promoted.restype = ctypes.c_int
+    lib.qattn_lowbit_workspace_bytes.argtypes = [P]
+    lib.qattn_lowbit_workspace_bytes.restype = sz
+    lib.qattn_block_mask_lowbit.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.qattn_block_mask_lowbit.restype = ctypes.c_int
     lib.qattn_head_error.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.qattn_head_error.restype = ctypes.c_int
     lib.qattn_fwd_adaptive.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -191,6 +195,24 @@ def qattn_fwd_promoted(p, q_i8, q_scale, k_i8, k_scale, q, k, k_mean, v, kv_idx,
                                    _stream(stream))
     if check:
         _check(st, "qattn_fwd_promoted")
+    return st
+
+
+def qattn_lowbit_workspace_bytes(p: qattn_problem_t) -> int:
+    return int(load().qattn_lowbit_workspace_bytes(ctypes.byref(p)))
+
+
+def qattn_block_mask_lowbit(p, q, k, k_mean, keep_num, keep_den, max_keep, kv_idx, kv_cnt,
+                            scores, workspace, workspace_bytes=None, stream=None,
+                            check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load().qattn_block_mask_lowbit(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_mean),
+                                        keep_num, keep_den, max_keep, _ptr(kv_idx),
+                                        _ptr(kv_cnt), _ptr(scores), _ptr(workspace),
+                                        workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "qattn_block_mask_lowbit")
     return st
 
 

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
-SOURCES = ["smooth_quant.hip", "block_mask.hip", "attn_fwd.hip", "head_error.hip", "api.cpp"]
+SOURCES = ["smooth_quant.hip", "block_mask.hip", "attn_fwd.hip", "head_error.hip", "lowbit_mask.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

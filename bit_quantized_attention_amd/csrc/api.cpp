@@ -164,6 +164,33 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t qattn_lowbit_workspace_bytes(const qattn_problem_t* p) {
+  Shape s;
+  if (check_problem(p, &s) != QATTN_OK) return 0;
+  return qattn::lowbit_workspace_bytes(s, true);
+}
+
+qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, const void* k,
+                                       const float* k_mean, int32_t keep_num, int32_t keep_den,
+                                       int32_t max_keep, int32_t* kv_idx, int32_t* kv_cnt,
+                                       float* scores, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.nkb() > qattn::mask_max_nkb()) return QATTN_ERR_UNSUPPORTED;
+  if (!q || !k || !k_mean || !kv_idx || !kv_cnt || !workspace) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, k_mean, kv_idx, kv_cnt, scores, workspace};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (!ratio_ok(keep_num, keep_den)) return QATTN_ERR_ARG;
+  if (max_keep < max_keep_of(s, keep_num, keep_den)) return QATTN_ERR_ARG;
+  if (workspace_bytes < qattn::lowbit_workspace_bytes(s, true)) return QATTN_ERR_ARG;
+  return launched(qattn::launch_lowbit_mask(s, q, k, k_mean, keep_num, keep_den, max_keep, kv_idx,
+                                            kv_cnt, scores, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 qattn_status_t qattn_head_error(const qattn_problem_t* p, const int8_t* q_i8,
                                 const float* q_scale, const int8_t* k_i8, const float* k_scale,
                                 const void* q, const void* k, const float* k_mean,

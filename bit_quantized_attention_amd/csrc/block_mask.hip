@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_quant_kernel(const float* _
 
 struct SelArgs {
   MaskLayout L;
+  const float* scores;  // [B*Hq*nqb][nkb] when the scores come precomputed
   int32_t* kv_idx;
   int32_t* kv_cnt;
   int B, Hq, Hkv, group, nqb, nkb, causal, keep_num, keep_den, max_keep;
@@ -92,11 +93,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D, int SLOTS>
+// FROM_SCORES: the block scores are read from a.scores (the low-bit
+// estimator) instead of being formed from the pooled codes.
+template <int D, int SLOTS, bool FROM_SCORES>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   constexpr int KSTR = D + 16;  // padded LDS row: 16-byte reads of 8 rows hit distinct banks
-  __shared__ __attribute__((aligned(16))) int8_t kcodes[kJChunk * KSTR];
-  __shared__ float kscale[kJChunk];
+  __shared__ __attribute__((aligned(16))) int8_t kcodes[FROM_SCORES ? 16 : kJChunk * KSTR];
+  __shared__ float kscale[FROM_SCORES ? 1 : kJChunk];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
     const size_t row = ((size_t)b * a.Hq + hq) * a.nqb + i;
     int32_t qw[D / 4];
     float qs = 1.0f;
-    if (active) {
+    if (active && !FROM_SCORES) {
       const int32_t* qsrc = reinterpret_cast<const int32_t*>(a.L.qc + row * D);
 #pragma unroll
       for (int w = 0; w < D / 4; ++w) qw[w] = qsrc[w];
@@ -127,7 +130,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
 #pragma unroll
     for (int u = 0; u < SLOTS; ++u) sc[u] = 0.0f;
 
-    for (int j0 = 0; j0 < nvalid; j0 += kJChunk) {
+    if constexpr (FROM_SCORES) {
+      if (active) {
+#pragma unroll
+        for (int u = 0; u < SLOTS; ++u) {
+          const int j = lane + 64 * u;
+          if (j < nvalid) sc[u] = a.scores[row * a.nkb + j];
+        }
+      }
+    }
+    for (int j0 = 0; j0 < (FROM_SCORES ? 0 : nvalid); j0 += kJChunk) {
       const int jn = min(kJChunk, nvalid - j0);
       __syncthreads();
       {
@@ -233,23 +245,43 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelArgs a) {
   }
 }
 
-template <int D, int SLOTS>
+template <int D, int SLOTS, bool FROM_SCORES>
 void launch_select(const SelArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((select_kernel<D, SLOTS>), dim3(grid), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL((select_kernel<D, SLOTS, FROM_SCORES>), dim3(grid), dim3(kSelThreads), 0,
+                     stream, a);
 }
 
-template <int D>
+template <int D, bool FROM_SCORES>
 void launch_select_d(const SelArgs& a, int grid, hipStream_t stream) {
   const int slots = (a.nkb + 63) / 64;
   if (slots <= 4) {
-    launch_select<D, 4>(a, grid, stream);
+    launch_select<D, 4, FROM_SCORES>(a, grid, stream);
   } else if (slots <= 8) {
-    launch_select<D, 8>(a, grid, stream);
+    launch_select<D, 8, FROM_SCORES>(a, grid, stream);
   } else if (slots <= 16) {
-    launch_select<D, 16>(a, grid, stream);
+    launch_select<D, 16, FROM_SCORES>(a, grid, stream);
   } else {
-    launch_select<D, 32>(a, grid, stream);
+    launch_select<D, 32, FROM_SCORES>(a, grid, stream);
   }
+}
+
+SelArgs sel_args(const Shape& s, int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
+                 int32_t* kv_cnt) {
+  SelArgs a;
+  a.scores = nullptr;
+  a.kv_idx = kv_idx;
+  a.kv_cnt = kv_cnt;
+  a.B = s.B;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.group = s.Hq / s.Hkv;
+  a.nqb = s.nqb();
+  a.nkb = s.nkb();
+  a.causal = s.causal;
+  a.keep_num = keep_num;
+  a.keep_den = keep_den;
+  a.max_keep = max_keep;
+  return a;
 }
 
 }  // namespace
@@ -277,26 +309,26 @@ hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k
     hipLaunchKernelGGL(pool_quant_kernel<64>, dim3(pgrid), dim3(kPoolThreads), 0, stream, q_pool,
                        k_pool, L, nq, nk);
   }
-  SelArgs a;
+  SelArgs a = sel_args(s, keep_num, keep_den, max_keep, kv_idx, kv_cnt);
   a.L = L;
-  a.kv_idx = kv_idx;
-  a.kv_cnt = kv_cnt;
-  a.B = s.B;
-  a.Hq = s.Hq;
-  a.Hkv = s.Hkv;
-  a.group = s.Hq / s.Hkv;
-  a.nqb = s.nqb();
-  a.nkb = s.nkb();
-  a.causal = s.causal;
-  a.keep_num = keep_num;
-  a.keep_den = keep_den;
-  a.max_keep = max_keep;
   const int grid = s.B * s.Hkv * a.nqb;
   if (s.d == 128) {
-    launch_select_d<128>(a, grid, stream);
+    launch_select_d<128, false>(a, grid, stream);
   } else {
-    launch_select_d<64>(a, grid, stream);
+    launch_select_d<64, false>(a, grid, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_scores(const Shape& s, const float* scores, int keep_num, int keep_den,
+                                int max_keep, int32_t* kv_idx, int32_t* kv_cnt,
+                                hipStream_t stream) {
+  SelArgs a = sel_args(s, keep_num, keep_den, max_keep, kv_idx, kv_cnt);
+  a.L = MaskLayout{};
+  a.scores = scores;
+  const int grid = s.B * s.Hkv * a.nqb;
+  // the score-reading kernel does not depend on d; one instance serves both
+  launch_select_d<64, true>(a, grid, stream);
   return hipGetLastError();
 }
 

@@ -39,6 +39,23 @@ hipError_t launch_block_mask(const Shape& s, const float* q_pool, const float* k
                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
                              int32_t* kv_cnt, void* workspace, hipStream_t stream);
 
+// Kept lists from precomputed block scores [B*Hq*nqb][nkb] (the pooled
+// mask's selection rule).
+hipError_t launch_select_scores(const Shape& s, const float* scores, int keep_num, int keep_den,
+                                int max_keep, int32_t* kv_idx, int32_t* kv_cnt,
+                                hipStream_t stream);
+
+// Workspace of the element-level 4-bit estimator (MX FP4 Q and K codes and
+// exponents, plus the block scores unless the caller takes them).
+size_t lowbit_workspace_bytes(const Shape& s, bool with_scores);
+
+// The element-level 4-bit block scores and the kept lists chosen from them;
+// scores (optional) receives the block scores.
+hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, const float* k_mean,
+                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
+                              int32_t* kv_cnt, float* scores, void* workspace,
+                              hipStream_t stream);
+
 // Longest kept list qattn_fwd accepts (entries per query block); also the
 // most 64-key blocks (N / 64) the promoted path supports.
 int fwd_max_sparse_tiles();

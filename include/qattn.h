@@ -232,6 +232,44 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
                                   int32_t max_keep, void* o, float* lse, void* stream);
 
 /*
+ * qattn_block_mask_lowbit -- per query block, the key blocks to keep, scored
+ * from element-level 4-bit estimates.
+ *
+ * The SALE explainer (aibr.jp/archives/118208), sections 2 and 3: every
+ * query-key product is estimated with 4-bit quantized Q and K, the estimates
+ * are turned into a block-sparse plan, and the sink and local (vertical and
+ * slash) patterns are kept. This library computes, per (b, hq):
+ *   the raw Q and the smoothed K, Ks = fl32(K) - k_mean, in OCP MX FP4: per 32
+ *   consecutive channels a shared exponent E = floor(log2 amax) - 2 (at least
+ *   -127; -127 for an all-zero group) and E2M1 elements, x / 2^E rounded to
+ *   nearest-even on {0, .5, 1, 1.5, 2, 3, 4, 6} and saturated at 6;
+ *   est(q, k) = the dot product of the dequantized vectors (the matrix cores
+ *   accumulate it in fp32);
+ *   score[i, j] = max of est over the causally visible pairs of query block i
+ *   (128 rows) and key block j (64 keys);
+ *   kept = the rule of qattn_block_mask (first and diagonal blocks forced,
+ *   then the top ceil(|valid| * keep_num / keep_den) of the rest by score,
+ *   ties to the lower block index).
+ * In:  q [B,Hq,N,d], k [B,Hkv,N,d] in p->dtype; k_mean [B,Hkv,d] f32 from
+ *      qattn_smooth_quant.
+ * Out: kv_idx [B,Hq,N/128,max_keep] int32 (kept blocks ascending, then -1),
+ *      kv_cnt [B,Hq,N/128] int32; scores [B,Hq,N/128,N/64] f32 or NULL (only
+ *      the causally valid entries are written).
+ * workspace: at least qattn_lowbit_workspace_bytes(p) bytes of device memory,
+ *      overwritten; not to be shared with a concurrent call.
+ * Errors: NULL (scores may be NULL); SHAPE/UNSUPPORTED, also UNSUPPORTED when
+ *      N > 131072; ALIGN; ARG for the keep ratio, max_keep below
+ *      qattn_max_keep(p, keep_num, keep_den), or a small workspace; DEVICE.
+ */
+size_t qattn_lowbit_workspace_bytes(const qattn_problem_t* p);
+
+qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, const void* k,
+                                       const float* k_mean, int32_t keep_num, int32_t keep_den,
+                                       int32_t max_keep, int32_t* kv_idx, int32_t* kv_cnt,
+                                       float* scores, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
  * qattn_head_error -- per-head error proxy of the INT8 Q K^T (adaptive
  * per-head precision, data-free).
  *

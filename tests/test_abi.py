@@ -108,7 +108,15 @@ def _fa(p, **over):
                                  args["lse"], stream=0, check=False)
 
 
-@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa])
+def _lb(p, **over):
+    args = dict(q=A, k=A, km=A, num=1, den=10, mk=1000, idx=A, cnt=A, sc=None, ws=A, wsb=1 << 40)
+    args.update(over)
+    return qa.qattn_block_mask_lowbit(p, args["q"], args["k"], args["km"], args["num"], args["den"],
+                                      args["mk"], args["idx"], args["cnt"], args["sc"], args["ws"],
+                                      args["wsb"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa, _lb])
 def test_problem_validation(lib, call):
     assert call(_p(B=0)) == SHAPE
     assert call(_p(Hq=0)) == SHAPE
@@ -199,6 +207,24 @@ def test_fwd_adaptive_arguments(lib):
     assert _fa(_p(N=131072 + 128)) == UNSUP
 
 
+def test_block_mask_lowbit_arguments(lib):
+    p = _p(N=1024)
+    for name in ["q", "k", "km", "idx", "cnt", "ws"]:
+        assert _lb(p, **{name: None}) == NULL, name
+        assert _lb(p, **{name: A + 4}) == ALIGN, name
+    assert _lb(p, sc=A + 4) == ALIGN
+    assert _lb(p, num=-1) == ARG
+    assert _lb(p, den=0) == ARG
+    assert _lb(p, mk=qa.qattn_max_keep(p, 1, 10) - 1) == ARG
+    need = qa.qattn_lowbit_workspace_bytes(p)
+    assert _lb(p, wsb=need - 1) == ARG
+    assert _lb(_p(N=131072 + 128)) == UNSUP
+    # FP4 codes and exponents of Q (4 heads) and K (2 heads), 256-byte aligned,
+    # plus the block scores
+    n_q, n_k = 4 * 1024, 2 * 1024
+    assert need == (n_q * 64 + n_q * 4 + n_k * 64 + n_k * 4) + 4 * 8 * 16 * 4
+
+
 def test_max_keep_and_workspace_sizes(lib):
     p = _p(N=32768, Hq=32, Hkv=8)
     assert qa.qattn_max_keep(p, 1, 10) == 55
@@ -213,7 +239,8 @@ def test_max_keep_and_workspace_sizes(lib):
 
 def test_binding_has_the_c_names():
     for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
-              "qattn_head_error", "qattn_fwd_adaptive", "qattn_workspace_bytes", "qattn_max_keep",
+              "qattn_head_error", "qattn_fwd_adaptive", "qattn_block_mask_lowbit",
+              "qattn_lowbit_workspace_bytes", "qattn_workspace_bytes", "qattn_max_keep",
               "qattn_status_str", "qattn_version"]:
         assert callable(getattr(qa, n))
 
