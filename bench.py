@@ -1,7 +1,7 @@
 """Benchmark of the quantized attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
-                    [--promote | --adaptive TAU]
+                    [--promote | --adaptive TAU] [--mask pooled|lowbit]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -23,6 +23,10 @@ mask keeps (the workload's keep ratio, else first + diagonal + top 10 %) run at
 algorithmic operations are those of the dense problem (4*d per visible pair),
 of which 2*d per promoted pair and 2*d per pair for P V are 16-bit; the peak
 is the matrix bound of that mix (INT8 and 16-bit work each at its own peak).
+
+With ``--mask lowbit`` the kept lists come from qattn_block_mask_lowbit (the
+element-level 4-bit estimator) instead of qattn_block_mask (pooled block
+means); the mask launch is part of the step either way.
 
 With ``--adaptive TAU`` the step runs qattn_head_error after the smoothing
 (its per-head INT8 logit error on a fixed sample) and then qattn_fwd_adaptive:
@@ -118,6 +122,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--promote", action="store_true",
                     help="promote the kept blocks to 16-bit Q K^T instead of skipping the rest")
+    ap.add_argument("--mask", choices=["pooled", "lowbit"], default="pooled",
+                    help="block scores from pooled block means or element-level 4-bit estimates")
     ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
                     help="per-head precision: heads whose sampled INT8 logit error exceeds TAU "
                          "(log2 units) run at 16-bit Q K^T")
@@ -151,7 +157,8 @@ def sparse_pairs(kv_idx: np.ndarray, kv_cnt: np.ndarray, causal: bool) -> float:
     return float(total)
 
 
-def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None):
+def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None,
+                     mask: str = "pooled"):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -175,7 +182,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         sparse = keep is not None
         sq = oracle.smooth_quant(q, k, pools=sparse)
         idx = cnt = None
-        if sparse:
+        if sparse and mask == "pooled":
             num, den = keep
             idx, cnt, _ = oracle.block_mask(sq["q_pool"], sq["k_pool"], len(hqs), 1, p.causal,
                                             num, den)
@@ -185,6 +192,10 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
             idx, cnt = oracle.adaptive_lists(err > adaptive, p.N, p.causal)
         for n in range(len(hqs)):
             blocks = [(0, n, i) for i in range(nqb)]
+            if sparse and mask == "lowbit":
+                idx, cnt, _, _ = oracle.lowbit_block_mask(q, k, len(hqs), 1, p.causal, keep[0],
+                                                          keep[1], k_mean=sq["k_mean"],
+                                                          heads=[(0, n)])
             if promote or adaptive is not None:
                 oracle.emulate_promoted_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                   sq["k_scale"], q, k, sq["k_mean"], v, p.causal,
@@ -209,7 +220,8 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         "unit": "TOPS (algorithmic)",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"oracle smooth_quant + {'block_mask + ' if sparse else ''}"
+        "sample": f"oracle smooth_quant + "
+                  f"{('lowbit_block_mask + ' if mask == 'lowbit' else 'block_mask + ') if sparse else ''}"
                   f"{'head_error + ' if adaptive is not None else ''}"
                   f"{'emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention'} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
@@ -247,6 +259,17 @@ def main():
     o = torch.empty_like(q)
     head_err = torch.empty((p.B, p.Hq), dtype=torch.float32, device=dev)
     head_hi = torch.empty((p.B, p.Hq), dtype=torch.int32, device=dev)
+    lowbit_ws = None
+    if args.mask == "lowbit" and keep is not None:
+        lowbit_ws = torch.empty(qa.qattn_lowbit_workspace_bytes(plan.p), dtype=torch.uint8,
+                                device=dev)
+
+    def block_mask():
+        if lowbit_ws is not None:
+            qa.qattn_block_mask_lowbit(plan.p, q, k, plan.k_mean, keep[0], keep[1], plan.max_keep,
+                                       plan.kv_idx, plan.kv_cnt, None, lowbit_ws)
+        else:
+            plan.block_mask()
 
     def head_precision():
         qa.qattn_head_error(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, q, k,
@@ -265,7 +288,7 @@ def main():
     for _ in range(args.warmup):
         plan.smooth_quant(q, k)
         if keep is not None:
-            plan.block_mask()
+            block_mask()
         if adaptive:
             head_precision()
         attention()
@@ -283,7 +306,7 @@ def main():
         sq_ev[s][0].record(stream)
         plan.smooth_quant(q, k)
         if keep is not None:
-            plan.block_mask()
+            block_mask()
         if adaptive:
             head_precision()
         sq_ev[s][1].record(stream)
@@ -363,7 +386,8 @@ def main():
                    "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
                    "causal": p.causal, "sparse": None if (args.promote or adaptive) else p.sparse,
                    "promote": list(keep) if args.promote else None,
-                   "adaptive_threshold": args.adaptive, "input_dtype": p.dtype},
+                   "adaptive_threshold": args.adaptive,
+                   "mask": args.mask if keep is not None else None, "input_dtype": p.dtype},
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
@@ -390,7 +414,7 @@ def main():
         res["adaptive" if adaptive else "promote"] = promote_info
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote,
-                                               args.adaptive)
+                                               args.adaptive, args.mask)
     print(json.dumps(res))
 
 

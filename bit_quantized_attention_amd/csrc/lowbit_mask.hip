@@ -18,6 +18,8 @@
 //      its second and later reads hit the CU's cache.
 //   3. the pooled mask's selection (forced + top fraction, ties to the lower
 //      block index) on these scores.
+#include <type_traits>
+
 #include "../../include/qattn.h"
 #include "device_util.h"
 #include "qattn_internal.h"
@@ -152,9 +154,11 @@ __global__ __launch_bounds__(256) void lowbit_score_kernel(ScoreArgs a) {
       }
     }
     float* out = a.L.scores + (bhq * a.nqb + i) * a.nkb;
-    for (int j = 0; j < nvalid; ++j) {
-      float best = -__builtin_inff();
-      const bool diag = a.causal && kKBlock * j + kKBlock - 1 > kQBlock * i;  // wave-uniform
+    // Per key block: the masked (diagonal) blocks take the element test, the
+    // others none; four running maxima per lane keep the max chains short.
+    auto score_block = [&](int j, auto diag_c) {
+      constexpr bool DIAG = decltype(diag_c)::value;
+      float best[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // A operand: key 64 j + 32 kb + l32
@@ -180,12 +184,22 @@ __global__ __launch_bounds__(256) void lowbit_score_kernel(ScoreArgs a) {
           const int lim = (32 * rb + l32) + kQBlock * i - (kKBlock * j + 32 * kb + 4 * h);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int off = 8 * (r >> 2) + (r & 3);
-            const float v = (diag && off > lim) ? -__builtin_inff() : s[r];
-            best = __builtin_fmaxf(best, v);
+            float v = s[r];
+            if constexpr (DIAG) {
+              const int off = 8 * (r >> 2) + (r & 3);
+              v = off > lim ? -__builtin_inff() : v;
+            }
+            best[r & 3] = __builtin_fmaxf(best[r & 3], v);
           }
         }
       }
+      return __builtin_fmaxf(__builtin_fmaxf(best[0], best[1]), __builtin_fmaxf(best[2], best[3]));
+    };
+    // the last key blocks of a causal query block need the element test
+    const int nplain = a.causal ? min(nvalid, (kQBlock * i + 1) / kKBlock) : nvalid;
+    for (int j = 0; j < nvalid; ++j) {
+      float best = j < nplain ? score_block(j, std::integral_constant<bool, false>{})
+                              : score_block(j, std::integral_constant<bool, true>{});
       best = wave_max(best);
       if (lane == 0) out[j] = best;
     }
