@@ -22,6 +22,10 @@ written for reading, not for speed:
 * ``lowbit_block_mask`` (module ``lowbit``) -- the element-level 4-bit
   block estimator: MX FP4 Q and smoothed K, the block score as the largest
   estimated product over the block's visible pairs, the same selection rule.
+* ``stripe_select`` / ``emulate_stripe_attention`` (module ``stripes``) --
+  anchor-based stripe selection (keys within a threshold of the anchor taken
+  over the initial tokens and the local window) and the quantized path over
+  the gathered keys.
 * ``head_error`` / ``adaptive_lists`` -- adaptive per-head precision: a
   sampled RMS logit error of the INT8 path per head, and the kept lists that
   run the heads above a threshold entirely at 16-bit Q K^T.
@@ -34,6 +38,9 @@ Sources (the explainer pages these follow):
 * ThriftAttention summary, gist.science/ja/paper/2605.23081, technical summary,
   method: block importance from the dot product of the block mean vectors,
   top-k block pairs, online softmax merge as in FlashAttention-2.
+* AnchorAttention explainer, aibr.jp/archives/118418, section 3: an anchor
+  from the initial tokens and a local window, keys selected by their
+  difference to it without a sort, discrete key gathers.
 * SALE explainer, aibr.jp/archives/118208, sections 1-3: a cheap low-bit
   estimate turned into a block-sparse plan that skips the rest, with the sink
   (first) and local (diagonal) stripes kept; element-level 4-bit estimates of
@@ -54,3 +61,4 @@ from .attention import (exact_attention, emulate_attention, emulate_promoted_att
                         promote_plan, softmax_scale_log2, head_error, head_error_sample,
                         adaptive_lists)
 from .lowbit import lowbit_block_mask, lowbit_scores, mxfp4_quantize  # noqa: F401,E402
+from .stripes import stripe_select, emulate_stripe_attention  # noqa: F401,E402
