@@ -1,7 +1,7 @@
 """Benchmark of the quantized attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
-                    [--promote | --adaptive TAU] [--mask pooled|lowbit]
+                    [--promote | --adaptive TAU | --stripes THETA] [--mask pooled|lowbit]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -32,6 +32,13 @@ With ``--adaptive TAU`` the step runs qattn_head_error after the smoothing
 (its per-head INT8 logit error on a fixed sample) and then qattn_fwd_adaptive:
 the heads whose error exceeds TAU take 16-bit Q K^T on every block, the rest
 INT8. Operations and peak are counted the same way.
+
+With ``--stripes THETA`` the step is qattn_smooth_quant, qattn_stripe_select
+(each query block keeps the first 64 keys, its own 128 positions and every key
+whose pooled score comes within THETA of the anchor, up to --stripe-keys keys)
+and qattn_fwd_stripes over the gathered keys. Its algorithmic operations are
+4*d per visible (query, listed key) pair, against the INT8 peak as for the
+dense and block-sparse paths.
 """
 
 from __future__ import annotations
@@ -75,13 +82,12 @@ def kernel_code_hash() -> str:
     return h.hexdigest()
 
 
-def counted_traffic(cfg: int, promote: bool = False):
+def counted_traffic(cfg: int, kind: str = "attn_fwd"):
     """HBM-side bytes per attn_fwd launch from the committed counter summary of
-    this workload (profiles/attn_fwd[_promoted]_<slug>_traffic.txt): FETCH_SIZE and
+    this workload (profiles/<kind>_<slug>_traffic.txt): FETCH_SIZE and
     WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain
     copy of known size. None when there is no summary or when the kernel code
     has changed since the counters were taken (its hash is recorded)."""
-    kind = "attn_fwd_promoted" if promote else "attn_fwd"
     path = os.path.join(ROOT, "profiles", f"{kind}_{SLUG[cfg]}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -127,6 +133,11 @@ def parse():
     ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
                     help="per-head precision: heads whose sampled INT8 logit error exceeds TAU "
                          "(log2 units) run at 16-bit Q K^T")
+    ap.add_argument("--stripes", type=float, default=None, metavar="THETA",
+                    help="anchor-based stripes: keep the keys whose pooled score is within THETA "
+                         "of the anchor and attend over the gathered keys")
+    ap.add_argument("--stripe-keys", type=int, default=3072,
+                    help="capacity of a query block's stripe key list (192..3072)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -157,8 +168,21 @@ def sparse_pairs(kv_idx: np.ndarray, kv_cnt: np.ndarray, causal: bool) -> float:
     return float(total)
 
 
+def stripe_pairs(key_idx: np.ndarray, key_cnt: np.ndarray, causal: bool) -> float:
+    """Visible (query, key) pairs under stripe key lists [B,Hq,nqb,mk]: a listed
+    key k of query block i is seen by the block's rows r >= k (causal)."""
+    B, H, nqb, mk = key_idx.shape
+    valid = np.arange(mk)[None, None, None, :] < key_cnt[..., None]
+    if causal:
+        r0 = 128 * np.arange(nqb, dtype=np.int64)[None, None, :, None]
+        vis = np.clip(r0 + 128 - np.maximum(key_idx.astype(np.int64), r0), 0, 128)
+    else:
+        vis = np.full(key_idx.shape, 128, dtype=np.int64)
+    return float(np.where(valid, vis, 0).sum())
+
+
 def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None,
-                     mask: str = "pooled"):
+                     mask: str = "pooled", stripes=None):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -180,7 +204,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         k = t["k"][b:b + 1, hk:hk + 1].contiguous()
         v = t["v"][b:b + 1, hk:hk + 1].contiguous()
         sparse = keep is not None
-        sq = oracle.smooth_quant(q, k, pools=sparse)
+        sq = oracle.smooth_quant(q, k, pools=sparse or stripes is not None)
         idx = cnt = None
         if sparse and mask == "pooled":
             num, den = keep
@@ -196,7 +220,14 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
                 idx, cnt, _, _ = oracle.lowbit_block_mask(q, k, len(hqs), 1, p.causal, keep[0],
                                                           keep[1], k_mean=sq["k_mean"],
                                                           heads=[(0, n)])
-            if promote or adaptive is not None:
+            if stripes is not None:
+                theta, mk = stripes
+                sidx, scnt, _ = oracle.stripe_select(sq["q_pool"][:, n:n + 1], sq["k_i8"],
+                                                     sq["k_scale"], 1, 1, p.causal, theta, mk)
+                oracle.emulate_stripe_attention(sq["q_i8"][:, n:n + 1], sq["q_scale"][:, n:n + 1],
+                                                sq["k_i8"], sq["k_scale"], v, p.causal, 1, 1,
+                                                sidx, scnt)
+            elif promote or adaptive is not None:
                 oracle.emulate_promoted_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                   sq["k_scale"], q, k, sq["k_mean"], v, p.causal,
                                                   len(hqs), 1, idx, cnt, blocks=blocks)
@@ -205,7 +236,9 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
                                          p.causal, len(hqs), 1, kv_idx=idx, kv_cnt=cnt,
                                          blocks=blocks)
             heads_done += 1
-            if sparse and not promote and adaptive is None:
+            if stripes is not None:
+                done_ops += 4.0 * p.d * stripe_pairs(sidx, scnt, p.causal)
+            elif sparse and not promote and adaptive is None:
                 done_ops += 4.0 * p.d * sparse_pairs(idx[:, n:n + 1], cnt[:, n:n + 1], p.causal)
             else:
                 pairs = p.N * (p.N + 1) / 2 if p.causal else float(p.N) ** 2
@@ -223,7 +256,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         "sample": f"oracle smooth_quant + "
                   f"{('lowbit_block_mask + ' if mask == 'lowbit' else 'block_mask + ') if sparse else ''}"
                   f"{'head_error + ' if adaptive is not None else ''}"
-                  f"{'emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention'} "
+                  f"{'stripe_select + emulate_stripe_attention' if stripes is not None else ('emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention')} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
                   f"({el:.1f} s); numpy BLAS {blas}",
     }
@@ -247,18 +280,22 @@ def main():
     p, t = make_config(args.config)
     dev = torch.device("cuda:0")
     q, k, v = (t[x].to(dev) for x in "qkv")
-    if args.promote and args.adaptive is not None:
-        raise SystemExit("--promote and --adaptive are exclusive")
+    if sum([args.promote, args.adaptive is not None, args.stripes is not None]) > 1:
+        raise SystemExit("--promote, --adaptive and --stripes are exclusive")
     adaptive = args.adaptive is not None
-    if adaptive:
+    stripes = args.stripes is not None
+    if adaptive or stripes:
         keep = None
     else:
         keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
-                   sparse=keep, promote=args.promote)
+                   sparse=keep, promote=args.promote, pools=True if stripes else None)
     o = torch.empty_like(q)
     head_err = torch.empty((p.B, p.Hq), dtype=torch.float32, device=dev)
     head_hi = torch.empty((p.B, p.Hq), dtype=torch.int32, device=dev)
+    nqb = p.N // 128
+    key_idx = torch.empty((p.B, p.Hq, nqb, args.stripe_keys), dtype=torch.int32, device=dev)
+    key_cnt = torch.empty((p.B, p.Hq, nqb), dtype=torch.int32, device=dev)
     lowbit_ws = None
     if args.mask == "lowbit" and keep is not None:
         lowbit_ws = torch.empty(qa.qattn_lowbit_workspace_bytes(plan.p), dtype=torch.uint8,
@@ -275,8 +312,15 @@ def main():
         qa.qattn_head_error(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, q, k,
                             plan.k_mean, args.adaptive, head_err, head_hi)
 
+    def stripe_select():
+        qa.qattn_stripe_select(plan.p, plan.q_pool, plan.k_i8, plan.k_scale, args.stripes,
+                               args.stripe_keys, key_idx, key_cnt)
+
     def attention():
-        if args.promote:
+        if stripes:
+            qa.qattn_fwd_stripes(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
+                                 key_idx, key_cnt, args.stripe_keys, o, plan.lse)
+        elif args.promote:
             plan.fwd_promoted(q, k, v, o)
         elif adaptive:
             qa.qattn_fwd_adaptive(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, q,
@@ -291,6 +335,8 @@ def main():
             block_mask()
         if adaptive:
             head_precision()
+        if stripes:
+            stripe_select()
         attention()
     torch.cuda.synchronize()
 
@@ -309,6 +355,8 @@ def main():
             block_mask()
         if adaptive:
             head_precision()
+        if stripes:
+            stripe_select()
         sq_ev[s][1].record(stream)
         ev[s][0].record(stream)
         attention()
@@ -359,6 +407,14 @@ def main():
                                  "heads": int(head_hi.numel()),
                                  "head_error_min": float(he.min()),
                                  "head_error_max": float(he.max())})
+    elif stripes:
+        pairs = stripe_pairs(key_idx.cpu().numpy(), key_cnt.cpu().numpy(), p.causal)
+        alg = 4.0 * p.d * pairs
+        vis = p.N * (p.N + 1) / 2 if p.causal else float(p.N) ** 2
+        promote_info = {"theta": args.stripes, "max_keys": args.stripe_keys,
+                        "kept_pair_fraction": pairs / (vis * p.Hq * p.B),
+                        "mean_list_length": float(key_cnt.float().mean().item()),
+                        "lists_at_capacity": int((key_cnt == args.stripe_keys).sum().item())}
     elif p.sparse is not None:
         pairs = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
         alg = 4.0 * p.d * pairs
@@ -382,11 +438,15 @@ def main():
         "data": "synthetic (seeded Gaussian Q/K/V with per-channel K offsets and outlier channels)",
         "config": {"workload": p.name + (" (kept blocks promoted to 16-bit QK^T, the rest INT8)"
                                          if args.promote else "") +
-                   (f" (per-head precision, error threshold {args.adaptive})" if adaptive else ""),
+                   (f" (per-head precision, error threshold {args.adaptive})" if adaptive else "") +
+                   (f" (anchor stripes, threshold {args.stripes}, up to {args.stripe_keys} keys)"
+                    if stripes else ""),
                    "B": p.B, "Hq": p.Hq, "Hkv": p.Hkv, "N": p.N, "d": p.d,
-                   "causal": p.causal, "sparse": None if (args.promote or adaptive) else p.sparse,
+                   "causal": p.causal,
+                   "sparse": None if (args.promote or adaptive or stripes) else p.sparse,
                    "promote": list(keep) if args.promote else None,
                    "adaptive_threshold": args.adaptive,
+                   "stripes": [args.stripes, args.stripe_keys] if stripes else None,
                    "mask": args.mask if keep is not None else None, "input_dtype": p.dtype},
         "roofline": {
             "bound": "mfma",
@@ -394,7 +454,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": counted_traffic(args.config, args.promote),
+            "traffic": counted_traffic(args.config, "attn_fwd_stripes" if stripes else
+                                       "attn_fwd_promoted" if args.promote else "attn_fwd"),
             "kernel": "attn_fwd",
             "algorithmic_ops_per_launch": alg,
             "avg_launch_ms": fwd_avg,
@@ -404,17 +465,18 @@ def main():
         "fwd_tops_algorithmic": achieved,
         "preprocess_ms": float(pre_ms.mean()),
         "preprocess_gbs_algorithmic": pre_bytes / (float(pre_ms.mean()) * 1e-3) / 1e9
-        if keep is None else None,
+        if keep is None and not adaptive and not stripes else None,
         "fwd_ms_median": float(np.median(fwd_ms)),
         "smooth_quant_ms_cache_flushed": pre_flushed_ms,
         "smooth_quant_gbs_cache_flushed": pre_bytes / (pre_flushed_ms * 1e-3) / 1e9,
         "blended_mfma_peak_tops": 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS),
     }
     if promote_info is not None:
-        res["adaptive" if adaptive else "promote"] = promote_info
+        res["adaptive" if adaptive else "stripes" if stripes else "promote"] = promote_info
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote,
-                                               args.adaptive, args.mask)
+                                               args.adaptive, args.mask,
+                                               (args.stripes, args.stripe_keys) if stripes else None)
     print(json.dumps(res))
 
 

@@ -81,6 +81,10 @@ def load(path: str = LIB_PATH):
     lib.qattn_lowbit_workspace_bytes.restype = sz
     lib.qattn_block_mask_lowbit.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.qattn_block_mask_lowbit.restype = ctypes.c_int
+    lib.qattn_stripe_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, vp, vp]
+    lib.qattn_stripe_select.restype = ctypes.c_int
+    lib.qattn_fwd_stripes.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.qattn_fwd_stripes.restype = ctypes.c_int
     lib.qattn_head_error.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.qattn_head_error.restype = ctypes.c_int
     lib.qattn_fwd_adaptive.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -213,6 +217,26 @@ def qattn_block_mask_lowbit(p, q, k, k_mean, keep_num, keep_den, max_keep, kv_id
                                         workspace_bytes, _stream(stream))
     if check:
         _check(st, "qattn_block_mask_lowbit")
+    return st
+
+
+def qattn_stripe_select(p, q_pool, k_i8, k_scale, theta, max_keys, key_idx, key_cnt,
+                        stream=None, check=True) -> int:
+    st = load().qattn_stripe_select(ctypes.byref(p), _ptr(q_pool), _ptr(k_i8), _ptr(k_scale),
+                                    float(theta), max_keys, _ptr(key_idx), _ptr(key_cnt),
+                                    _stream(stream))
+    if check:
+        _check(st, "qattn_stripe_select")
+    return st
+
+
+def qattn_fwd_stripes(p, q_i8, q_scale, k_i8, k_scale, v, key_idx, key_cnt, max_keys, o,
+                      lse=None, stream=None, check=True) -> int:
+    st = load().qattn_fwd_stripes(ctypes.byref(p), _ptr(q_i8), _ptr(q_scale), _ptr(k_i8),
+                                  _ptr(k_scale), _ptr(v), _ptr(key_idx), _ptr(key_cnt), max_keys,
+                                  _ptr(o), _ptr(lse), _stream(stream))
+    if check:
+        _check(st, "qattn_fwd_stripes")
     return st
 
 

@@ -19,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
 SOURCES = ["smooth_quant.hip", "block_mask.hip", "attn_fwd.hip", "head_error.hip", "lowbit_mask.hip",
+           "stripes.hip",
            "api.cpp"]
 ARCH = "gfx950"
 

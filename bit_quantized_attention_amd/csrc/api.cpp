@@ -139,7 +139,7 @@ qattn_status_t qattn_fwd(const qattn_problem_t* p, const int8_t* q_i8, const flo
   if (kv_idx != nullptr && (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()))
     return QATTN_ERR_ARG;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
-                                         max_keep, nullptr, nullptr, nullptr, nullptr, o, lse,
+                                         max_keep, nullptr, nullptr, nullptr, nullptr, false, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -160,7 +160,7 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
     if (x && misaligned(x)) return QATTN_ERR_ALIGN;
   if (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()) return QATTN_ERR_ARG;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, kv_idx, kv_cnt,
-                                         max_keep, q, k, k_mean, nullptr, o, lse,
+                                         max_keep, q, k, k_mean, nullptr, false, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -189,6 +189,45 @@ qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, 
   return launched(qattn::launch_lowbit_mask(s, q, k, k_mean, keep_num, keep_den, max_keep, kv_idx,
                                             kv_cnt, scores, workspace,
                                             static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_stripe_select(const qattn_problem_t* p, const float* q_pool,
+                                   const int8_t* k_i8, const float* k_scale, float theta,
+                                   int32_t max_keys, int32_t* key_idx, int32_t* key_cnt,
+                                   void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.N > 65536) return QATTN_ERR_UNSUPPORTED;
+  if (!q_pool || !k_i8 || !k_scale || !key_idx || !key_cnt) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_pool, k_i8, k_scale, key_idx, key_cnt};
+  for (const void* x : ptrs)
+    if (misaligned(x)) return QATTN_ERR_ALIGN;
+  if (std::isnan(theta)) return QATTN_ERR_ARG;
+  // the anchor region (up to 64 + 128 keys) always fits
+  if (max_keys < QATTN_K_BLOCK + QATTN_Q_BLOCK || max_keys > qattn::fwd_max_gather_keys())
+    return QATTN_ERR_ARG;
+  return launched(qattn::launch_stripe_select(s, q_pool, k_i8, k_scale, theta, max_keys, key_idx,
+                                              key_cnt, static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_fwd_stripes(const qattn_problem_t* p, const int8_t* q_i8,
+                                 const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                 const void* v, const int32_t* key_idx, const int32_t* key_cnt,
+                                 int32_t max_keys, void* o, float* lse, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.N > 65536) return QATTN_ERR_UNSUPPORTED;
+  if (!q_i8 || !q_scale || !k_i8 || !k_scale || !v || !key_idx || !key_cnt || !o)
+    return QATTN_ERR_NULL;
+  const void* ptrs[] = {q_i8, q_scale, k_i8, k_scale, v, key_idx, key_cnt, o, lse};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (max_keys < 1 || max_keys > qattn::fwd_max_gather_keys()) return QATTN_ERR_ARG;
+  return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, key_idx, key_cnt,
+                                         max_keys, nullptr, nullptr, nullptr, nullptr, true, o,
+                                         lse, static_cast<hipStream_t>(stream)));
 }
 
 qattn_status_t qattn_head_error(const qattn_problem_t* p, const int8_t* q_i8,
@@ -225,7 +264,7 @@ qattn_status_t qattn_fwd_adaptive(const qattn_problem_t* p, const int8_t* q_i8,
   for (const void* x : ptrs)
     if (x && misaligned(x)) return QATTN_ERR_ALIGN;
   return launched(qattn::launch_attn_fwd(s, q_i8, q_scale, k_i8, k_scale, v, nullptr, nullptr, 0,
-                                         q, k, k_mean, head_hi, o, lse,
+                                         q, k, k_mean, head_hi, false, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 

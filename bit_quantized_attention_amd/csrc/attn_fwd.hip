@@ -71,6 +71,8 @@ constexpr float kSBiasF = 12582912.0f;
 // the reference by more than kTau; only then is the row max computed.
 constexpr float kSumFilter = 128.0f;
 constexpr int kMaxSparseTiles = 2048;
+// longest gathered key list (64-key tiles of listed keys) per query block
+constexpr int kMaxGatherKeys = 3072;
 
 template <bool BF16>
 struct Mma16;
@@ -125,6 +127,9 @@ struct FwdArgs {
   const uint16_t* k16;
   const float* k_mean;
   const int32_t* head_hi;
+  // kv_idx / kv_cnt / max_keep hold key lists (gathered keys) instead of
+  // block lists
+  bool gather;
   int B, Hq, Hkv, N, group, g4, nqb, nkb, max_keep;
   float c;  // fl32(log2(e) / sqrt(d))
 };
@@ -178,7 +183,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF, bool PROMOTE>
+template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF, bool PROMOTE,
+          bool GATHER>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
@@ -192,6 +198,9 @@ void attn_fwd_kernel(FwdArgs a) {
   // promoted path: sparse layout (one 128-row query block per workgroup),
   // one 32-query block per wave
   static_assert(!PROMOTE || (SPARSE && QB == 1), "promoted path: sparse layout, QB = 1");
+  // gathered keys: sparse layout; kv_idx holds key lists (max_keep entries per
+  // query block) and a tile is 64 consecutive list entries
+  static_assert(!GATHER || (SPARSE && QB == 1 && !PROMOTE), "gathered keys: sparse layout, QB = 1");
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
   // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
@@ -216,7 +225,8 @@ void attn_fwd_kernel(FwdArgs a) {
   };
   auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
-  __shared__ int16_t tile_list[SPARSE ? kMaxSparseTiles : 1];
+  __shared__ int16_t tile_list[SPARSE && !GATHER ? kMaxSparseTiles : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t key_list[GATHER ? kMaxGatherKeys : 1];
   __shared__ uint32_t kept_bits[PROMOTE ? kMaxSparseTiles / 32 : 1];
   __shared__ int n_list, n_list_plain, n_list_hi;
 
@@ -318,6 +328,37 @@ void attn_fwd_kernel(FwdArgs a) {
     ntiles = n_list;
     n_plain = n_list_plain;
     n_hi = n_list_hi;
+  } else if constexpr (GATHER) {
+    // the key list (entries outside [0, N) or past the causal range dropped,
+    // order kept); tiles are 64 consecutive entries. The unmasked tiles are
+    // the whole tiles before the first entry past the workgroup's first row.
+    if (wave == 0) {
+      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxGatherKeys));
+      const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      int n = 0, first_late = INT_MAX;
+      for (int e0 = 0; e0 < cnt; e0 += 64) {
+        const int e = e0 + lane;
+        const int k = e < cnt ? src[e] : -1;
+        const bool ok = k >= 0 && k < a.N && (!CAUSAL || k <= wg_last_row);
+        const uint64_t bal = __ballot(ok);
+        const int pos = n + __popcll(bal & lt);
+        if (ok) key_list[pos] = (uint16_t)k;
+        const uint64_t late = __ballot(ok && CAUSAL && k > wg_row0);
+        if (late != 0ull && first_late == INT_MAX) {
+          const int l0 = __builtin_ctzll(late);
+          first_late = n + __popcll(bal & ((l0 == 0) ? 0ull : (~0ull >> (64 - l0))));
+        }
+        n += __popcll(bal);
+      }
+      if (lane == 0) {
+        n_list = n;
+        n_list_plain = min(first_late, n) / kKT;
+      }
+    }
+    __syncthreads();
+    ntiles = (n_list + kKT - 1) / kKT;
+    n_plain = n_list_plain;
   } else if constexpr (SPARSE) {
     if (wave == 0) {
       const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
@@ -346,8 +387,15 @@ void attn_fwd_kernel(FwdArgs a) {
     n_plain = CAUSAL ? min(ntiles, (wg_row0 + 1) / kKT) : ntiles;
   }
   auto tile_of = [&](int it) -> int {
-    if constexpr (SPARSE) return tile_list[it];
+    if constexpr (SPARSE && !GATHER) return tile_list[it];
     else return it;
+  };
+  // gathered keys: the key of list entry pos (entries past the list read its
+  // last key, an empty list key 0: valid rows whose results are masked)
+  const int n_keys = GATHER ? n_list : 0;
+  auto listed_key = [&](int pos) -> int {
+    if constexpr (GATHER) return n_keys > 0 ? (int)key_list[min(pos, n_keys - 1)] : 0;
+    else return 0;
   };
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------------
@@ -409,6 +457,29 @@ void attn_fwd_kernel(FwdArgs a) {
   auto tile_kscale = [&](const int8_t* buf) {
     return *reinterpret_cast<const float*>(buf + G::KBUF);
   };
+  // gathered tile t: row r of the K and V tiles is listed key 64 t + r
+  auto load_k_gather = [&](int t, int8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int piece = (wave + NW * j) % KPIECES;
+      const int r = piece * (1024 / G::KROW) + lane / G::KSLOTS;
+      const int key = listed_key(kKT * t + r);
+      const int8_t* src = a.k_i8 + (kv_row0 + (size_t)key) * D +
+                          (((lane % G::KSLOTS) ^ G::kswz(r)) * 16);
+      lds_dma16(src, buf + piece * 1024);
+    }
+  };
+  auto load_v_gather = [&](int t, int8_t* buf) {
+#pragma unroll
+    for (int j = 0; j < VPW; ++j) {
+      const int piece = (wave + NW * j) % VPIECES;
+      const int r = piece * (1024 / G::VROW) + lane / G::VSLOTS;
+      const int key = listed_key(kKT * t + r);
+      const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)key) * D) +
+                          (((lane % G::VSLOTS) ^ G::vswz(r)) * 16);
+      lds_dma16(src, buf + piece * 1024);
+    }
+  };
   auto load_v = [&](int t, int8_t* buf) {
     const int8_t* src = reinterpret_cast<const int8_t*>(a.v + (kv_row0 + (size_t)t * kKT) * D);
 #pragma unroll
@@ -463,6 +534,13 @@ void attn_fwd_kernel(FwdArgs a) {
   // wait. (A promoted half loads it too, unused, so that every step issues
   // the same number of loads.)
   auto issue = [&](int t, int hs, int8_t* kb, int8_t* vb) {
+    if constexpr (GATHER) {
+      // lane l brings the scale of row l's key into the tail
+      load_k_gather(t, kb);
+      lds_dma4(kscale + listed_key(kKT * t + lane) / kKT, kb + G::KBUF);
+      load_v_gather(t, vb);
+      return;
+    }
     if constexpr (PROMOTE) {
       if (hs >= 0) load_k16(t, hs, kb);
       else load_k(t, kb);
@@ -777,6 +855,95 @@ void attn_fwd_kernel(FwdArgs a) {
     });
   };
 
+  // ---- gathered tiles: a scale per key ----------------------------------------
+  // Element (kb, r) of the lane's 32 keys is row kb*32 + 8*(r/4) + 4*h + r%4
+  // of the tile, i.e. list entry 64*it + that row. Its logit is
+  // fl32(S * fl32(alpha_q * sk)) with sk the row's scale from the tile tail;
+  // P = exp2(fl32(logit - m)). Masked tiles drop entries past the list and,
+  // under causal masking, keys past the row. Reference rule, filter and rescale as in softmax.
+  auto softmax_gather = [&](auto masked_c, const v16i (&s)[2][QB], const int8_t* kb_buf, int it,
+                            op_t (&pf)[2][QB][2]) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const float* tail = reinterpret_cast<const float*>(kb_buf + G::KBUF);
+    const int row = row0 + l32;
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int rr = kb * 32 + 8 * g4 + 4 * h;  // first of the 4 rows
+        const float4 sk4 = *reinterpret_cast<const float4*>(tail + rr);
+        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
+        int keyv[4] = {0, 0, 0, 0};
+        if constexpr (MASKED) {
+          const uint2 kw = *reinterpret_cast<const uint2*>(&key_list[kKT * it + rr]);
+          keyv[0] = (int)(kw.x & 0xffffu);
+          keyv[1] = (int)(kw.x >> 16);
+          keyv[2] = (int)(kw.y & 0xffffu);
+          keyv[3] = (int)(kw.y >> 16);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          const float S = __builtin_bit_cast(float, (int)s[kb][0][r]) - kSBiasF;  // exact
+          const float alpha = alpha_q * skv[e];
+          float v = S * alpha;
+          if constexpr (MASKED) {
+            if (kKT * it + rr + e >= n_keys || (CAUSAL && keyv[e] > row)) v = -__builtin_inff();
+          }
+          x[kb][r] = v;
+        }
+      }
+    auto exps = [&](float m) -> float {
+      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          op_t pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float pe = __builtin_amdgcn_exp2f(x[kb][8 * hf + e] - m);
+            // a dropped element gives 0 also while m is still -inf (where
+            // -inf - m would give NaN), as in the block softmax
+            if constexpr (MASKED) pe = x[kb][8 * hf + e] == -__builtin_inff() ? 0.0f : pe;
+            lsum[e & 3] += pe;
+            pk[e] = (el_t)pe;
+          }
+          pf[kb][0][hf] = pk;
+        }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    float psum = exps(m_ref[0]);
+    if (__ballot(psum > kSumFilter) != 0) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, x[kb][r]);
+      {
+        const int mi = __builtin_bit_cast(int, mx);
+        const auto sw = __builtin_amdgcn_permlane32_swap(mi, mi, false, false);
+        mx = __builtin_fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+      }
+      const float m_old = m_ref[0];
+      const float mc = __builtin_fmaxf(m_old, mx);
+      const bool move = mc > m_old + kTau;
+      if (__ballot(move) != 0) {
+        const float corr =
+            move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
+        m_ref[0] = move ? mc : m_old;
+        psum = exps(m_ref[0]);
+        l_run[0] *= corr;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][0][r] *= corr;
+      }
+    }
+    l_run[0] += psum;
+  };
+
   // ---- pipeline ---------------------------------------------------------------------
   // Tile j's K (with its scale) and V live in buffer j % NBUF. Iteration it
   // issues the loads of tile it+PD into buffer (it+PD) % NBUF, whose last
@@ -869,13 +1036,14 @@ void attn_fwd_kernel(FwdArgs a) {
       }
     } else {
       if (wave_live) {
-        alpha = alpha_q * tile_kscale(kbuf(cur));
+        if constexpr (!GATHER) alpha = alpha_q * tile_kscale(kbuf(cur));
         qk(kbuf(cur), s);
       }
       issue(tl, tl_hs, kbuf(nxt), vbuf(nxt));
       if (wave_live) {
         op_t p[2][QB][2];
-        softmax(masked_c, s, alpha, t, p, [](auto, auto) {});
+        if constexpr (GATHER) softmax_gather(masked_c, s, kbuf(cur), it, p);
+        else softmax(masked_c, s, alpha, t, p, [](auto, auto) {});
         pv(vbuf(cur), p);
       }
     }
@@ -1028,19 +1196,23 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
   static_assert(NW_DENSE % 4 == 0, "whole waves per SIMD");
   if (sparse) {
     const dim3 grid(a.B * a.Hq * a.nqb);
-    if (a.q16 != nullptr) {
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, true>), grid, dim3(4 * 64),
-                         0, stream, a);
+    if (a.gather) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, false, true>), grid,
+                         dim3(4 * 64), 0, stream, a);
+    } else if (a.q16 != nullptr) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, true, false>), grid,
+                         dim3(4 * 64), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3, false>), grid,
-                         dim3(NW_SPARSE * 64), 0, stream, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, QB, NW_SPARSE, 2, 3, false, false>),
+                         grid, dim3(NW_SPARSE * 64), 0, stream, a);
     }
   } else {
     const int rows_wg = 32 * QBD * (NW_DENSE / a.g4);
     const int nrc = (a.N + rows_wg - 1) / rows_wg;
     const dim3 grid(a.B * a.Hkv * (a.group / a.g4) * nrc);
     constexpr int NBUF_DENSE = NW_DENSE * QBD >= 8 ? 4 : 3;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE, false>),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, false, QBD, NW_DENSE, WPE_DENSE, NBUF_DENSE, false,
+                                        false>),
                        grid, dim3(NW_DENSE * 64), 0, stream, a);
   }
   return hipGetLastError();
@@ -1055,12 +1227,14 @@ hipError_t launch_d(const FwdArgs& a, bool causal, bool sparse, hipStream_t stre
 }  // namespace
 
 int fwd_max_sparse_tiles() { return kMaxSparseTiles; }
+int fwd_max_gather_keys() { return kMaxGatherKeys; }
 
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
                            const void* q16, const void* k16, const float* k_mean,
-                           const int32_t* head_hi, void* o, float* lse, hipStream_t stream) {
+                           const int32_t* head_hi, bool gather, void* o, float* lse,
+                           hipStream_t stream) {
   FwdArgs a;
   a.q_i8 = q_i8;
   a.q_scale = q_scale;
@@ -1075,6 +1249,7 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
   a.k16 = static_cast<const uint16_t*>(k16);
   a.k_mean = k_mean;
   a.head_hi = head_hi;
+  a.gather = gather;
   a.B = s.B;
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;

@@ -61,13 +61,23 @@ hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, cons
 int fwd_max_sparse_tiles();
 
 // Dense (kv_idx NULL), sparse (kv_idx set, q16 NULL), promoted (kv_idx, q16,
-// k16 and k_mean set) or adaptive (head_hi, q16, k16 and k_mean set, kv_idx
-// NULL) attention forward.
+// k16 and k_mean set), adaptive (head_hi, q16, k16 and k_mean set, kv_idx
+// NULL) or gathered-key (gather, kv_idx / kv_cnt / max_keep the key lists)
+// attention forward.
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
                            const void* q16, const void* k16, const float* k_mean,
-                           const int32_t* head_hi, void* o, float* lse, hipStream_t stream);
+                           const int32_t* head_hi, bool gather, void* o, float* lse,
+                           hipStream_t stream);
+
+// Longest key list the gathered-key forward accepts (entries per query block).
+int fwd_max_gather_keys();
+
+// Anchor-based stripe selection: key lists [B*Hq*nqb][max_keys] and counts.
+hipError_t launch_stripe_select(const Shape& s, const float* q_pool, const int8_t* k_i8,
+                                const float* k_scale, float theta, int max_keys,
+                                int32_t* key_idx, int32_t* key_cnt, hipStream_t stream);
 
 // Per-head sampled RMS logit error of the INT8 path against the 16-bit path;
 // head_hi (optional) gets err > threshold.

@@ -270,6 +270,59 @@ qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, 
                                        void* stream);
 
 /*
+ * qattn_stripe_select -- per query block, the key positions within a
+ * threshold of the anchor (AnchorAttention-style stripes).
+ *
+ * The AnchorAttention explainer (aibr.jp/archives/118418), section 3: an
+ * approximate maximum score (the anchor) from the initial tokens and a local
+ * window; every other position is kept when its score comes within a
+ * threshold of the anchor, by direct comparison without a sort, selecting
+ * discrete key positions. This library computes, per (b, hq, query block i):
+ *   score(k) = fl32(fl32(dot * sq) * sk[k/64]): dot the exact product of the
+ *     INT8 codes of the block's mean query (q_pool, quantized on its own as in
+ *     qattn_block_mask) and of key k (k_i8), sk = k_scale;
+ *   region = the first 64 keys and keys 128 i .. 128 i + 127, causally valid;
+ *   anchor = max of score over the region;
+ *   kept = region + { k causally valid : score(k) >= fl32(anchor - theta) },
+ *     ascending; when that exceeds max_keys, the region and the lowest-index
+ *     other keys.
+ * In:  q_pool [B,Hq,N/128,d] f32, k_i8 [B,Hkv,N,d], k_scale [B,Hkv,N/64] from
+ *      qattn_smooth_quant; theta (score units, may be +inf).
+ * Out: key_idx [B,Hq,N/128,max_keys] int32 (ascending, then -1),
+ *      key_cnt [B,Hq,N/128] int32.
+ * Errors: NULL; SHAPE/UNSUPPORTED, also UNSUPPORTED when N > 65536; ALIGN;
+ *      ARG when theta is NaN or max_keys is outside [192, 3072]; DEVICE.
+ */
+qattn_status_t qattn_stripe_select(const qattn_problem_t* p, const float* q_pool,
+                                   const int8_t* k_i8, const float* k_scale, float theta,
+                                   int32_t max_keys, int32_t* key_idx, int32_t* key_cnt,
+                                   void* stream);
+
+/*
+ * qattn_fwd_stripes -- quantized attention over gathered (discrete) keys.
+ *
+ * The AnchorAttention explainer (aibr.jp/archives/118418), section 3: the
+ * attention reads the selected discrete key and value positions instead of
+ * contiguous blocks. This library computes qattn_fwd's online softmax per
+ * query block over its key list taken 64 entries at a time (the last group
+ * may be shorter), in list order, with each key's own block scale:
+ *   s = fl32(S * fl32(fl32(q_scale * fl32(log2(e)/sqrt(d))) * k_scale[k/64])),
+ *   -inf where the key is past the row (causal).
+ * In:  q_i8, q_scale, k_i8, k_scale from qattn_smooth_quant; v; key_idx /
+ *      key_cnt (e.g. from qattn_stripe_select; entries outside [0, N) or past
+ *      the query block's causal range and counts above max_keys are ignored;
+ *      lists should be ascending: the first whole 64-entry groups holding no
+ *      key past the block's first row skip the causal test).
+ * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
+ * Errors: NULL; SHAPE/UNSUPPORTED, also UNSUPPORTED when N > 65536; ALIGN;
+ *      ARG when max_keys is outside [1, 3072]; DEVICE.
+ */
+qattn_status_t qattn_fwd_stripes(const qattn_problem_t* p, const int8_t* q_i8,
+                                 const float* q_scale, const int8_t* k_i8, const float* k_scale,
+                                 const void* v, const int32_t* key_idx, const int32_t* key_cnt,
+                                 int32_t max_keys, void* o, float* lse, void* stream);
+
+/*
  * qattn_head_error -- per-head error proxy of the INT8 Q K^T (adaptive
  * per-head precision, data-free).
  *

@@ -116,7 +116,22 @@ def _lb(p, **over):
                                       args["wsb"], stream=0, check=False)
 
 
-@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa, _lb])
+def _ss(p, **over):
+    args = dict(qp=A, ki=A, ks=A, th=1.0, mk=512, idx=A, cnt=A)
+    args.update(over)
+    return qa.qattn_stripe_select(p, args["qp"], args["ki"], args["ks"], args["th"], args["mk"],
+                                  args["idx"], args["cnt"], stream=0, check=False)
+
+
+def _fs(p, **over):
+    args = dict(qi=A, qs=A, ki=A, kscl=A, v=A, idx=A, cnt=A, mk=512, o=A, lse=None)
+    args.update(over)
+    return qa.qattn_fwd_stripes(p, args["qi"], args["qs"], args["ki"], args["kscl"], args["v"],
+                                args["idx"], args["cnt"], args["mk"], args["o"], args["lse"],
+                                stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa, _lb, _ss, _fs])
 def test_problem_validation(lib, call):
     assert call(_p(B=0)) == SHAPE
     assert call(_p(Hq=0)) == SHAPE
@@ -225,6 +240,24 @@ def test_block_mask_lowbit_arguments(lib):
     assert need == (n_q * 64 + n_q * 4 + n_k * 64 + n_k * 4) + 4 * 8 * 16 * 4
 
 
+def test_stripe_arguments(lib):
+    p = _p(N=1024)
+    for name in ["qp", "ki", "ks", "idx", "cnt"]:
+        assert _ss(p, **{name: None}) == NULL, name
+        assert _ss(p, **{name: A + 4}) == ALIGN, name
+    assert _ss(p, th=float("nan")) == ARG
+    assert _ss(p, mk=191) == ARG
+    assert _ss(p, mk=3073) == ARG
+    assert _ss(_p(N=65536 + 128)) == UNSUP
+    for name in ["qi", "qs", "ki", "kscl", "v", "idx", "cnt", "o"]:
+        assert _fs(p, **{name: None}) == NULL, name
+        assert _fs(p, **{name: A + 8}) == ALIGN, name
+    assert _fs(p, lse=A + 4) == ALIGN
+    assert _fs(p, mk=0) == ARG
+    assert _fs(p, mk=3073) == ARG
+    assert _fs(_p(N=65536 + 128)) == UNSUP
+
+
 def test_max_keep_and_workspace_sizes(lib):
     p = _p(N=32768, Hq=32, Hkv=8)
     assert qa.qattn_max_keep(p, 1, 10) == 55
@@ -240,7 +273,8 @@ def test_max_keep_and_workspace_sizes(lib):
 def test_binding_has_the_c_names():
     for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
               "qattn_head_error", "qattn_fwd_adaptive", "qattn_block_mask_lowbit",
-              "qattn_lowbit_workspace_bytes", "qattn_workspace_bytes", "qattn_max_keep",
+              "qattn_lowbit_workspace_bytes", "qattn_stripe_select", "qattn_fwd_stripes",
+              "qattn_workspace_bytes", "qattn_max_keep",
               "qattn_status_str", "qattn_version"]:
         assert callable(getattr(qa, n))
 

@@ -1,0 +1,126 @@
+"""GPU parity of the anchor-based stripe path (qattn_stripe_select and
+qattn_fwd_stripes) against the oracle, through the C ABI.
+
+The selection uses exact integer dot products and the same two fp32
+roundings as the oracle, so the key lists are compared bit for bit. The
+forward over the gathered keys is compared with the oracle's emulation under
+the oracle's own lists, at the bars of the other paths.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.stripes import emulate_stripe_attention, stripe_select
+from synthetic import make_case
+from parity_util import TOL_EMU, COS_MIN, KERNEL_TAU, log, out_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("bf16-d128-causal-gqa4-N2048", dict(B=1, Hq=8, Hkv=2, N=2048, d=128, dtype="bf16",
+                                         causal=True, seed=101, k_offset_std=3.0, outliers=4),
+     1.0, 512),
+    ("f16-d64-nc-B2-N640", dict(B=2, Hq=4, Hkv=4, N=640, d=64, dtype="f16", causal=False,
+                                seed=102, k_offset_std=2.0), 1.5, 640),
+    ("bf16-d64-causal-mqa-N1024-tight", dict(B=1, Hq=4, Hkv=1, N=1024, d=64, dtype="bf16",
+                                             causal=True, seed=103, k_offset_std=3.0),
+     3.0, 256),
+    ("bf16-d128-causal-N4096", dict(B=1, Hq=2, Hkv=1, N=4096, d=128, dtype="bf16", causal=True,
+                                    seed=104, k_offset_std=3.0, outliers=4), 0.5, 1024),
+]
+
+
+def _gpu(qa, p, t, theta, max_keys):
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev, pools=True,
+                   with_lse=True)
+    plan.smooth_quant(q, k)
+    nqb = p.N // 128
+    idx = torch.empty((p.B, p.Hq, nqb, max_keys), dtype=torch.int32, device=dev)
+    cnt = torch.empty((p.B, p.Hq, nqb), dtype=torch.int32, device=dev)
+    qa.qattn_stripe_select(plan.p, plan.q_pool, plan.k_i8, plan.k_scale, theta, max_keys, idx, cnt)
+    o = torch.empty_like(q)
+    qa.qattn_fwd_stripes(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v, idx, cnt,
+                         max_keys, o, plan.lse)
+    torch.cuda.synchronize()
+    return plan, idx, cnt, o
+
+
+@pytest.mark.parametrize("name,kw,theta,max_keys", CASES, ids=[c[0] for c in CASES])
+def test_stripes_select_bit_exact_and_fwd_matches_emulation(gpu_lib, name, kw, theta, max_keys):
+    p, t = make_case(**kw)
+    log(f"stripes {name} theta={theta} max_keys={max_keys}")
+    plan, idx, cnt, o = _gpu(gpu_lib, p, t, theta, max_keys)
+    sq = oracle.smooth_quant(t["q"], t["k"], pools=True)
+    o_idx, o_cnt, _ = stripe_select(sq["q_pool"], sq["k_i8"], sq["k_scale"], p.Hq, p.Hkv,
+                                    p.causal, theta, max_keys)
+    assert np.array_equal(to_np(cnt), o_cnt)
+    assert np.array_equal(to_np(idx), o_idx)
+    frac = float(o_cnt.sum()) / (p.B * p.Hq * (p.N // 128) * p.N)
+    _, O_pre, lse_emu = emulate_stripe_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
+                                                 sq["k_scale"], t["v"], p.causal, p.Hq, p.Hkv,
+                                                 o_idx, o_cnt, tau=KERNEL_TAU)
+    e = out_err(to_np(o), O_pre, p.dtype)
+    dl = float(np.abs(to_np(plan.lse) - lse_emu).max())
+    log(f"  lists bit-exact (kept fraction {frac:.3f}); err_vs_emu={e:.3e} lse_err={dl:.2e}")
+    assert e <= TOL_EMU and dl < 1e-4
+
+
+def test_stripes_fwd_hand_made_lists(gpu_lib):
+    # entries out of range or past the causal range are dropped, a partial last
+    # group of 64 entries is masked, an empty list gives O = 0 and lse = -inf
+    p, t = make_case(B=1, Hq=2, Hkv=1, N=1024, d=128, dtype="bf16", causal=True, seed=105,
+                     k_offset_std=3.0)
+    log("stripes fwd, hand-made lists")
+    dev = torch.device("cuda:0")
+    qa = gpu_lib
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev, with_lse=True)
+    plan.smooth_quant(q, k)
+    nqb, mk = p.N // 128, 300
+    rng = np.random.default_rng(3)
+    idx = np.full((1, 2, nqb, mk), -1, dtype=np.int32)
+    cnt = np.zeros((1, 2, nqb), dtype=np.int32)
+    for h in range(2):
+        for i in range(nqb):
+            if h == 1 and i == 2:
+                continue  # empty list
+            keys = sorted(rng.choice(128 * i + 128, min(128 * i + 128, 150), replace=False))
+            keys = [-5] + list(keys) + [5000, 128 * i + 300]  # invalid entries
+            idx[0, h, i, :len(keys)] = keys
+            cnt[0, h, i] = len(keys)
+    o = torch.empty_like(q)
+    qa.qattn_fwd_stripes(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
+                         torch.from_numpy(idx).to(dev), torch.from_numpy(cnt).to(dev), mk, o,
+                         plan.lse)
+    torch.cuda.synchronize()
+    clean_idx = np.full_like(idx, -1)
+    clean_cnt = np.zeros_like(cnt)
+    for h in range(2):
+        for i in range(nqb):
+            keep = [x for x in idx[0, h, i, :cnt[0, h, i]] if 0 <= x <= 128 * i + 127]
+            clean_idx[0, h, i, :len(keep)] = keep
+            clean_cnt[0, h, i] = len(keep)
+    sq = oracle.smooth_quant(t["q"], t["k"])
+    _, O_pre, lse_emu = emulate_stripe_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
+                                                 sq["k_scale"], t["v"], True, 2, 1, clean_idx,
+                                                 clean_cnt, tau=KERNEL_TAU)
+    og, lse = to_np(o), to_np(plan.lse)
+    empty = np.zeros((1, 2, p.N), dtype=bool)
+    empty[0, 1, 256:384] = True
+    assert np.all(og[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    assert out_err(og[~empty], O_pre[~empty], p.dtype) <= TOL_EMU
+    assert np.abs(lse[~empty] - lse_emu[~empty]).max() < 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_stripes_v_ones(gpu_lib, dtype):
+    p, t = make_case(B=1, Hq=4, Hkv=2, N=1024, d=64, dtype=dtype, causal=True, seed=106,
+                     k_offset_std=2.0)
+    t1 = dict(t, v=torch.ones_like(t["v"]))
+    _, _, _, o = _gpu(gpu_lib, p, t1, 1.0, 512)
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    assert torch.all((o.double() - 1.0).abs() <= u)
