@@ -337,19 +337,28 @@ void attn_fwd_kernel(FwdArgs a) {
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       int n = 0, first_late = INT_MAX;
-      for (int e0 = 0; e0 < cnt; e0 += 64) {
-        const int e = e0 + lane;
-        const int k = e < cnt ? src[e] : -1;
-        const bool ok = k >= 0 && k < a.N && (!CAUSAL || k <= wg_last_row);
-        const uint64_t bal = __ballot(ok);
-        const int pos = n + __popcll(bal & lt);
-        if (ok) key_list[pos] = (uint16_t)k;
-        const uint64_t late = __ballot(ok && CAUSAL && k > wg_row0);
-        if (late != 0ull && first_late == INT_MAX) {
-          const int l0 = __builtin_ctzll(late);
-          first_late = n + __popcll(bal & ((l0 == 0) ? 0ull : (~0ull >> (64 - l0))));
+      // eight 64-entry chunks per round, their loads all in flight together
+      for (int e0 = 0; e0 < cnt; e0 += 8 * 64) {
+        int kc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = e0 + 64 * j + lane;
+          kc[j] = e < cnt ? src[e] : -1;
         }
-        n += __popcll(bal);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int k = kc[j];
+          const bool ok = k >= 0 && k < a.N && (!CAUSAL || k <= wg_last_row);
+          const uint64_t bal = __ballot(ok);
+          const int pos = n + __popcll(bal & lt);
+          if (ok) key_list[pos] = (uint16_t)k;
+          const uint64_t late = __ballot(ok && CAUSAL && k > wg_row0);
+          if (late != 0ull && first_late == INT_MAX) {
+            const int l0 = __builtin_ctzll(late);
+            first_late = n + __popcll(bal & ((l0 == 0) ? 0ull : (~0ull >> (64 - l0))));
+          }
+          n += __popcll(bal);
+        }
       }
       if (lane == 0) {
         n_list = n;

@@ -124,3 +124,38 @@ def test_stripes_v_ones(gpu_lib, dtype):
     _, _, _, o = _gpu(gpu_lib, p, t1, 1.0, 512)
     u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
     assert torch.all((o.double() - 1.0).abs() <= u)
+
+
+def test_stripes_full_size_sampled(gpu_lib):
+    # the block-sparse workload's shape (B1 Hq32 Hkv8 N32768 d128 bf16, causal)
+    # at the stripe bench's settings: the lists of two query heads of the last
+    # kv group bit-exact over every query block, and the forward on sampled
+    # blocks within the bar of its emulation
+    from synthetic import make_config
+    from parity_util import head_slice
+    p, t = make_config(5)
+    theta, mk = 1.0, 3072
+    log(f"stripes full size: {p.name}, theta={theta}, max_keys={mk}")
+    plan, idx, cnt, o = _gpu(gpu_lib, p, t, theta, mk)
+    b, hk = 0, p.Hkv - 1
+    hqs = [hk * p.group, hk * p.group + p.group - 1]
+    sub, _ = head_slice(t, p, b, hqs)
+    ref = oracle.smooth_quant(sub["q"], sub["k"], pools=True)
+    o_idx, o_cnt, _ = stripe_select(ref["q_pool"], ref["k_i8"], ref["k_scale"], len(hqs), 1,
+                                    p.causal, theta, mk)
+    g_idx = to_np(idx)[b, hqs][None]
+    g_cnt = to_np(cnt)[b, hqs][None]
+    assert np.array_equal(g_cnt, o_cnt)
+    assert np.array_equal(g_idx, o_idx)
+    nqb = p.N // 128
+    blocks = [0, nqb // 2, nqb - 1]
+    sel = [(0, n, i) for n in range(len(hqs)) for i in blocks]
+    _, O_pre, _ = emulate_stripe_attention(ref["q_i8"], ref["q_scale"], ref["k_i8"],
+                                           ref["k_scale"], sub["v"], p.causal, len(hqs), 1,
+                                           o_idx, o_cnt, blocks=sel, tau=KERNEL_TAU)
+    rows = np.concatenate([np.arange(i * 128, i * 128 + 128) for i in blocks])
+    g = to_np(o[b, hqs])[None][:, :, rows]
+    e = out_err(g, O_pre[:, :, rows], p.dtype)
+    log(f"  lists bit-exact (mean length {float(o_cnt.mean()):.0f}, "
+        f"{int((o_cnt == mk).sum())} at capacity); sampled err_vs_emu={e:.3e}")
+    assert e <= TOL_EMU
