@@ -333,22 +333,27 @@ void attn_fwd_kernel(FwdArgs a) {
     // order kept); tiles are 64 consecutive entries. The unmasked tiles are
     // the whole tiles before the first entry past the workgroup's first row.
     if (wave == 0) {
-      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxGatherKeys));
+      const int cap = min(a.max_keep, kMaxGatherKeys);
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
+      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], cap);
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       int n = 0, first_late = INT_MAX;
-      // eight 64-entry chunks per round, their loads all in flight together
-      for (int e0 = 0; e0 < cnt; e0 += 8 * 64) {
+      // eight 64-entry chunks per round, their loads all in flight together;
+      // the first round reads up to the row's capacity without waiting for
+      // the count (entries past it are masked below)
+      int e0 = 0;
+      do {
         int kc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int e = e0 + 64 * j + lane;
-          kc[j] = e < cnt ? src[e] : -1;
+          kc[j] = e < cap ? src[e] : -1;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int k = kc[j];
-          const bool ok = k >= 0 && k < a.N && (!CAUSAL || k <= wg_last_row);
+          const bool ok = e0 + 64 * j + lane < cnt && k >= 0 && k < a.N &&
+                          (!CAUSAL || k <= wg_last_row);
           const uint64_t bal = __ballot(ok);
           const int pos = n + __popcll(bal & lt);
           if (ok) key_list[pos] = (uint16_t)k;
@@ -359,7 +364,8 @@ void attn_fwd_kernel(FwdArgs a) {
           }
           n += __popcll(bal);
         }
-      }
+        e0 += 8 * 64;
+      } while (e0 < cnt);
       if (lane == 0) {
         n_list = n;
         n_list_plain = min(first_late, n) / kKT;
@@ -370,14 +376,18 @@ void attn_fwd_kernel(FwdArgs a) {
     n_plain = n_list_plain;
   } else if constexpr (SPARSE) {
     if (wave == 0) {
-      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], min(a.max_keep, kMaxSparseTiles));
+      const int cap = min(a.max_keep, kMaxSparseTiles);
       const int32_t* src = a.kv_idx + (bhq * a.nqb + qblk) * a.max_keep;
+      // the first 64 entries are read together with the count (the row holds
+      // max_keep entries) and serve both passes
+      const int t_first = lane < cap ? src[lane] : -1;
+      const int cnt = min(a.kv_cnt[bhq * a.nqb + qblk], cap);
       const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       int n = 0;
       for (int pass = 0; pass < 2; ++pass) {
         for (int e0 = 0; e0 < cnt; e0 += 64) {
           const int e = e0 + lane;
-          const int t = e < cnt ? src[e] : -1;
+          const int t = e >= cnt ? -1 : e0 == 0 ? t_first : src[e];
           const bool ok = t >= 0 && t < a.nkb && (!CAUSAL || t * kKT <= wg_last_row) &&
                           (masked(t) == (pass == 1));
           const uint64_t bal = __ballot(ok);
