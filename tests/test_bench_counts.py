@@ -1,0 +1,74 @@
+"""The bench's operation counts against brute force, and its one-GPU guard
+(host logic, no GPU)."""
+
+import json
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _pairs_brute(keys_per_block, N, causal):
+    total = 0
+    for i, keys in enumerate(keys_per_block):
+        for r in range(128 * i, 128 * i + 128):
+            total += sum(1 for k in keys if (k <= r or not causal))
+    return total
+
+
+def test_dense_ops():
+    for causal in (True, False):
+        p = SimpleNamespace(N=384, d=64, Hq=3, B=2, causal=causal)
+        pairs = _pairs_brute([range(384)] * 3, 384, causal)
+        assert bench.dense_algorithmic_ops(p) == 4.0 * 64 * pairs * 3 * 2
+
+
+def test_sparse_pairs():
+    rng = np.random.default_rng(0)
+    N, nqb, mk = 512, 4, 5
+    for causal in (True, False):
+        idx = np.full((1, 2, nqb, mk), -1, np.int32)
+        cnt = np.zeros((1, 2, nqb), np.int32)
+        want = 0
+        for h in range(2):
+            blocks_i = []
+            for i in range(nqb):
+                nvis = 2 * i + 2 if causal else N // 64
+                bl = sorted(rng.choice(nvis, min(nvis, 3), replace=False))
+                idx[0, h, i, :len(bl)] = bl
+                cnt[0, h, i] = len(bl)
+                blocks_i.append([k for b in bl for k in range(64 * b, 64 * b + 64)])
+            want += _pairs_brute(blocks_i, N, causal)
+        assert bench.sparse_pairs(idx, cnt, causal) == want
+
+
+def test_stripe_pairs():
+    rng = np.random.default_rng(1)
+    N, nqb, mk = 512, 4, 300
+    for causal in (True, False):
+        idx = np.full((2, 1, nqb, mk), -1, np.int32)
+        cnt = np.zeros((2, 1, nqb), np.int32)
+        want = 0
+        for b in range(2):
+            keys_i = []
+            for i in range(nqb):
+                nvis = 128 * i + 128 if causal else N
+                keys = sorted(rng.choice(nvis, min(nvis, 150), replace=False))
+                idx[b, 0, i, :len(keys)] = keys
+                cnt[b, 0, i] = len(keys)
+                keys_i.append(keys)
+            want += _pairs_brute(keys_i, N, causal)
+        assert bench.stripe_pairs(idx, cnt, causal) == want
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
