@@ -56,9 +56,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;             // keys per tile
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
@@ -80,29 +78,18 @@ struct Mma16;
 template <>
 struct Mma16<true> {
   typedef v8bf op_t;
-  typedef v2bf pair_t;
   typedef __bf16 el_t;
   static __device__ __forceinline__ v16f mma(op_t a, op_t b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  // sum of the two 16-bit values of a pair, accumulated in fp32
-  static __device__ __forceinline__ float sum2(pair_t p, float acc) {
-    const pair_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
   }
 };
 
 template <>
 struct Mma16<false> {
   typedef v8h op_t;
-  typedef v2h pair_t;
   typedef _Float16 el_t;
   static __device__ __forceinline__ v16f mma(op_t a, op_t b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ float sum2(pair_t p, float acc) {
-    const pair_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(p, one, acc, false);
   }
 };
 
@@ -189,7 +176,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
   using op_t = typename MM::op_t;
-  using pair_t = typename MM::pair_t;
   using el_t = typename MM::el_t;
   using G = Geo<D>;
   constexpr int RW = 32 * QB;
