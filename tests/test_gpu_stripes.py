@@ -29,6 +29,20 @@ CASES = [
      3.0, 256),
     ("bf16-d128-causal-N4096", dict(B=1, Hq=2, Hkv=1, N=4096, d=128, dtype="bf16", causal=True,
                                     seed=104, k_offset_std=3.0, outliers=4), 0.5, 1024),
+    # three query heads per kv head: the 32 query vectors of a workgroup
+    # straddle query blocks unevenly
+    ("f16-d64-nc-group3-N384", dict(B=1, Hq=6, Hkv=2, N=384, d=64, dtype="f16", causal=False,
+                                    seed=107, k_offset_std=2.0), 0.5, 384),
+    # a single query block
+    ("bf16-d128-causal-B2-N128", dict(B=2, Hq=2, Hkv=1, N=128, d=128, dtype="bf16",
+                                      causal=True, seed=108), 1.0, 192),
+    # every visible key, and the anchor region alone
+    ("bf16-d64-causal-theta-inf", dict(B=1, Hq=2, Hkv=1, N=1024, d=64, dtype="bf16",
+                                       causal=True, seed=109, k_offset_std=3.0),
+     float("inf"), 1024),
+    ("bf16-d64-causal-theta-neg-inf", dict(B=1, Hq=2, Hkv=1, N=1024, d=64, dtype="bf16",
+                                           causal=True, seed=110, k_offset_std=3.0),
+     float("-inf"), 192),
 ]
 
 
@@ -59,6 +73,9 @@ def test_stripes_select_bit_exact_and_fwd_matches_emulation(gpu_lib, name, kw, t
                                     p.causal, theta, max_keys)
     assert np.array_equal(to_np(cnt), o_cnt)
     assert np.array_equal(to_np(idx), o_idx)
+    if theta == float("inf"):  # every causally visible key
+        nvis = np.minimum(128 * np.arange(p.N // 128) + 128, p.N) if p.causal else p.N
+        assert np.array_equal(o_cnt, np.broadcast_to(nvis, o_cnt.shape))
     frac = float(o_cnt.sum()) / (p.B * p.Hq * (p.N // 128) * p.N)
     _, O_pre, lse_emu = emulate_stripe_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                  sq["k_scale"], t["v"], p.causal, p.Hq, p.Hkv,
