@@ -213,6 +213,8 @@ void attn_fwd_kernel(FwdArgs a) {
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
   __shared__ int16_t tile_list[SPARSE && !GATHER ? kMaxSparseTiles : 1];
   __shared__ __attribute__((aligned(16))) uint16_t key_list[GATHER ? kMaxGatherKeys : 1];
+  // gathered tiles: each wave's fl32(alpha_q * k_scale) of the tile's 64 keys
+  __shared__ __attribute__((aligned(16))) float key_alpha[GATHER ? NW * 64 : 1];
   __shared__ uint32_t kept_bits[PROMOTE ? kMaxSparseTiles / 32 : 1];
   __shared__ int n_list, n_list_plain, n_list_hi;
 
@@ -871,14 +873,18 @@ void attn_fwd_kernel(FwdArgs a) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const float* tail = reinterpret_cast<const float*>(kb_buf + G::KBUF);
     const int row = row0 + l32;
+    // lane l forms key l's alpha once for the wave (its own LDS slot: the
+    // wave's reads below see its write)
+    float* wal = key_alpha + wave * 64;
+    wal[lane] = alpha_q * tail[lane];
     float x[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int rr = kb * 32 + 8 * g4 + 4 * h;  // first of the 4 rows
-        const float4 sk4 = *reinterpret_cast<const float4*>(tail + rr);
-        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
+        const float4 al4 = *reinterpret_cast<const float4*>(wal + rr);
+        const float alv[4] = {al4.x, al4.y, al4.z, al4.w};
         int keyv[4] = {0, 0, 0, 0};
         if constexpr (MASKED) {
           const uint2 kw = *reinterpret_cast<const uint2*>(&key_list[kKT * it + rr]);
@@ -891,7 +897,7 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g4 + e;
           const float S = __builtin_bit_cast(float, (int)s[kb][0][r]) - kSBiasF;  // exact
-          const float alpha = alpha_q * skv[e];
+          const float alpha = alv[e];
           float v = S * alpha;
           if constexpr (MASKED) {
             if (kKT * it + rr + e >= n_keys || (CAUSAL && keyv[e] > row)) v = -__builtin_inff();
