@@ -311,8 +311,9 @@ qattn_status_t qattn_stripe_select(const qattn_problem_t* p, const float* q_pool
  * In:  q_i8, q_scale, k_i8, k_scale from qattn_smooth_quant; v; key_idx /
  *      key_cnt (e.g. from qattn_stripe_select; entries outside [0, N) or past
  *      the query block's causal range and counts above max_keys are ignored;
- *      lists should be ascending: the first whole 64-entry groups holding no
- *      key past the block's first row skip the causal test).
+ *      a repeated entry is attended as often as it appears; lists should be
+ *      ascending: the first whole 64-entry groups holding no key past the
+ *      block's first row skip the causal test).
  * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
  * Errors: NULL; SHAPE/UNSUPPORTED, also UNSUPPORTED when N > 65536; ALIGN;
  *      ARG when max_keys is outside [1, 3072]; DEVICE.

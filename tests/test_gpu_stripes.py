@@ -87,8 +87,9 @@ def test_stripes_select_bit_exact_and_fwd_matches_emulation(gpu_lib, name, kw, t
 
 
 def test_stripes_fwd_hand_made_lists(gpu_lib):
-    # entries out of range or past the causal range are dropped, a partial last
-    # group of 64 entries is masked, an empty list gives O = 0 and lse = -inf
+    # entries out of range or past the causal range are dropped, a repeated
+    # entry counts as often as it appears, a partial last group of 64 entries
+    # is masked, an empty list gives O = 0 and lse = -inf
     p, t = make_case(B=1, Hq=2, Hkv=1, N=1024, d=128, dtype="bf16", causal=True, seed=105,
                      k_offset_std=3.0)
     log("stripes fwd, hand-made lists")
@@ -106,7 +107,8 @@ def test_stripes_fwd_hand_made_lists(gpu_lib):
             if h == 1 and i == 2:
                 continue  # empty list
             keys = sorted(rng.choice(128 * i + 128, min(128 * i + 128, 150), replace=False))
-            keys = [-5] + list(keys) + [5000, 128 * i + 300]  # invalid entries
+            # invalid entries, and a repeated last key (attended twice)
+            keys = [-5] + list(keys) + [keys[-1], 5000, 128 * i + 300]
             idx[0, h, i, :len(keys)] = keys
             cnt[0, h, i] = len(keys)
     o = torch.empty_like(q)
