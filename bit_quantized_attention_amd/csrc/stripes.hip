@@ -13,8 +13,9 @@
 // ahead. The score is the exact int32 product with two fp32 roundings, as in
 // the pooled mask. Per group the kept keys of each query vector become two
 // 32-bit masks (anchor-region keys, other kept keys); the waves swap their
-// masks through LDS, and prefix popcounts give every kept key its place in
-// the ascending list. Past the capacity only anchor-region keys are written.
+// masks' counts through LDS, and the counts of the waves before plus
+// popcounts within the wave's own masks give every kept key its place in the
+// ascending list. Past the capacity only anchor-region keys are written.
 #include "device_util.h"
 #include "qattn_internal.h"
 
@@ -62,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void stripe_select_kernel(StripeArgs a) {
   __shared__ __attribute__((aligned(16))) int8_t qcodes[kCols][D];
   __shared__ float qscale[kCols];
   __shared__ float thr_s[kCols];
-  __shared__ uint32_t mreg[2][kWaves][kCols];
-  __shared__ uint32_t moth[2][kWaves][kCols];
+  // per step, wave and column: anchor-region keys << 16 | other kept keys
+  __shared__ uint32_t mcnt[2][kWaves][kCols];
   __shared__ int cnt_s[kCols];
 
   const int lane = threadIdx.x & 63;
@@ -238,21 +239,20 @@ __global__ __launch_bounds__(kThreads) void stripe_select_kernel(StripeArgs a) {
     const uint32_t reg32 = both_halves(spread(reg16));
     const uint32_t oth32 = both_halves(spread(oth16));
     const int buf = it & 1;
-    if (h == 0) {
-      mreg[buf][wave][l32] = reg32;
-      moth[buf][wave][l32] = oth32;
-    }
+    // (at most 32 keys per group and wave: the packed sums cannot carry)
+    if (h == 0)
+      mcnt[buf][wave][l32] = ((uint32_t)__builtin_popcount(reg32) << 16) |
+                             (uint32_t)__builtin_popcount(oth32);
     barrier();
-    int rpre = 0, opre = 0, rtot = 0, otot = 0;
+    uint32_t pre = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const int rc = __builtin_popcount(mreg[buf][w][l32]);
-      const int oc = __builtin_popcount(moth[buf][w][l32]);
-      rpre += w < wave ? rc : 0;
-      opre += w < wave ? oc : 0;
-      rtot += rc;
-      otot += oc;
+      const uint32_t v = mcnt[buf][w][l32];
+      pre += w < wave ? v : 0u;
+      tot += v;
     }
+    const int rpre = (int)(pre >> 16), opre = (int)(pre & 0xFFFFu);
+    const int rtot = (int)(tot >> 16), otot = (int)(tot & 0xFFFFu);
     uint32_t mine = reg16 | oth16;
     while (mine != 0u) {
       const int r = __builtin_ctz(mine);
