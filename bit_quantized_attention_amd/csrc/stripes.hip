@@ -208,6 +208,7 @@ __global__ __launch_bounds__(kThreads) void stripe_select_kernel(StripeArgs a) {
     const int g = it * kWaves + wave;
     const int key0 = 32 * g;
     uint32_t reg16 = 0, oth16 = 0;
+    bool plain = true;  // no anchor-region key and no visibility test in the group
     if (g < ngroups) {  // wave-uniform
       v16i acc;
 #pragma unroll
@@ -215,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void stripe_select_kernel(StripeArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[ks], qf[ks], acc, 0, 0, 0);
       const float ksc = ksc_ref;
-      const bool plain = key0 >= kKBlock && (key0 + 32 <= win_lo || key0 >= win_hi) &&
-                         key0 + 32 <= nv_min;
+      plain = key0 >= kKBlock && (key0 + 32 <= win_lo || key0 >= win_hi) &&
+              key0 + 32 <= nv_min;
       if (plain) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void stripe_select_kernel(StripeArgs a) {
       }
     }
     load_k(min(g + 2 * kWaves, ngroups - 1), kf, ksc_ref);
-    const uint32_t reg32 = both_halves(spread(reg16));
+    const uint32_t reg32 = plain ? 0u : both_halves(spread(reg16));  // (uniform)
     const uint32_t oth32 = both_halves(spread(oth16));
     const int buf = it & 1;
     // (at most 32 keys per group and wave: the packed sums cannot carry)
