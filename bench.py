@@ -265,9 +265,9 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        print("bench.py: only --gpus 1 is supported (single-GPU build)", file=sys.stderr)
+        print("bench.py: only --gpus 1 is supported (single-GPU library)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
