@@ -14,7 +14,8 @@ import torch
 import oracle
 from oracle.lowbit import lowbit_block_mask
 from synthetic import make_case
-from parity_util import TOL_EMU, COS_MIN, KERNEL_TAU, log, out_err, cos, to_np
+from parity_util import (TOL_EMU, COS_MIN, KERNEL_TAU, log, out_err, cos, to_np, emulate_both,
+                         check_out)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,18 +81,18 @@ def test_lowbit_mask_drives_the_sparse_forward(gpu_lib):
     o_idx, o_cnt, _, _ = lowbit_block_mask(t["q"], t["k"], p.Hq, p.Hkv, True, keep[0], keep[1],
                                            mk)
     sq = oracle.smooth_quant(t["q"], t["k"])
-    _, pre_skip, _ = oracle.emulate_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
-                                              sq["k_scale"], t["v"], True, p.Hq, p.Hkv,
-                                              kv_idx=o_idx, kv_cnt=o_cnt, tau=KERNEL_TAU)
-    _, pre_prom, _ = oracle.emulate_promoted_attention(
-        sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], t["q"], t["k"], sq["k_mean"],
-        t["v"], True, p.Hq, p.Hkv, o_idx, o_cnt, tau=KERNEL_TAU)
+    (_, pre_skip, _), (_, pre_skip0, _) = emulate_both(
+        oracle.emulate_attention, sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], t["v"],
+        True, p.Hq, p.Hkv, kv_idx=o_idx, kv_cnt=o_cnt)
+    (_, pre_prom, _), (_, pre_prom0, _) = emulate_both(
+        oracle.emulate_promoted_attention, sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"],
+        t["q"], t["k"], sq["k_mean"], t["v"], True, p.Hq, p.Hkv, o_idx, o_cnt)
     ex_mask, _ = oracle.exact_attention(t["q"], t["k"], t["v"], True, o_idx, o_cnt)
-    e1 = out_err(to_np(o_skip), pre_skip, p.dtype)
-    e2 = out_err(to_np(o_prom), pre_prom, p.dtype)
+    check_out(to_np(o_skip), pre_skip, pre_skip0, p.dtype, "skip: ", v=t["v"])
+    check_out(to_np(o_prom), pre_prom, pre_prom0, p.dtype, "promoted: ", v=t["v"])
     c1 = cos(to_np(o_skip), ex_mask)
-    log(f"  skip err_vs_emu={e1:.3e} cos_exact_same_mask={c1:.6f}; promoted err_vs_emu={e2:.3e}")
-    assert e1 <= TOL_EMU and e2 <= TOL_EMU and c1 >= COS_MIN
+    log(f"  skip cos_exact_same_mask={c1:.6f}")
+    assert c1 >= COS_MIN
 
 
 def test_lowbit_finds_a_planted_element_the_pooled_mask_misses(gpu_lib):
