@@ -117,6 +117,56 @@ def copy_calibration(mib: int, reps: int):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": reps}))
 
 
+PEAK_KINDS = [
+    # (kind, param, name, unit of the rate, divisor to that unit)
+    (0, 0, "mfma_i8_32x32x32", "TOPS", 1e12),
+    (1, 0, "mfma_bf16_32x32x16", "TFLOP/s", 1e12),
+    (2, 0, "mfma_mix_1i8_2bf16", "TOPS", 1e12),
+    (3, 0, "valu_fma_f32", "G lane-instr/s", 1e9),
+    (4, 0, "valu_exp_f32", "G lane-instr/s", 1e9),
+    *[(5, n, f"coissue_bf16_mfma_plus_{n}_exp_1wave_per_simd", "TFLOP/s", 1e12)
+      for n in (0, 2, 4, 6, 8, 12, 16)],
+    *[(6, n, f"coissue_bf16_mfma_plus_{n}_fma_1wave_per_simd", "TFLOP/s", 1e12)
+      for n in (2, 4, 6, 8, 12, 16)],
+    *[(10, n, f"coissue_mfma16x16x32_bf16_plus_{n}_fma_1wave_per_simd", "TFLOP/s", 1e12)
+      for n in (0, 1, 2, 3, 4)],
+    *[(11, n, f"coissue_mfma_i8_plus_{n}_fma_1wave_per_simd", "TOPS", 1e12)
+      for n in (0, 2, 4, 6, 8)],
+    *[(12, n, f"split_waves_bf16_mfma_vs_{n}_fma_per_mfma", "TFLOP/s", 1e12)
+      for n in (0, 2, 4, 6, 8)],
+    *[(13, n, f"split_waves_bf16_mfma_vs_{n}_exp_per_mfma", "TFLOP/s", 1e12)
+      for n in (2, 4, 6)],
+    (7, 0, "lds_read_b128", "GB/s", 1e9),
+    (8, 0, "lds_read_b64_tr_b16", "GB/s", 1e9),
+    (9, 0, "hbm_copy_1gib_read_plus_write", "GB/s", 1e9),
+]
+
+
+def run_peaks():
+    """The peak-rate micro-benchmarks of libqattn_peaks.so, one JSON line each:
+    the rate, the kernel time, the shader clock under that load and the cycles
+    one loop iteration of the first wave took (its own s_memtime)."""
+    import ctypes
+    import torch
+    from bit_quantized_attention_amd import build as _b
+    torch.cuda.init()
+    lib = ctypes.CDLL(_b.PEAKS_LIB)
+    lib.qattn_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.qattn_peak.restype = ctypes.c_int
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for kind, param, name, unit, div in PEAK_KINDS:
+        res = (ctypes.c_double * 4)()
+        rc = lib.qattn_peak(kind, param, res)
+        if rc != 0:
+            raise SystemExit(f"peak benchmark {name} failed with HIP error {rc}")
+        rate, ms, ghz, cyc = res[0], res[1], res[2], res[3]
+        line = {"peak": name, "rate": rate / div, "unit": unit, "kernel_ms": ms,
+                "clock_ghz": ghz, "cycles_per_iteration_wave0": cyc}
+        if ghz > 0:
+            line["per_cu_per_clock"] = rate / (ncu * ghz * 1e9)
+        print(json.dumps(line), flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +190,8 @@ def parse():
                     help="capacity of a query block's stripe key list (192..3072)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the peak-rate micro-benchmarks (matrix, vector, LDS, HBM)")
     return ap.parse_args()
 
 
@@ -271,6 +323,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
+    if args.peaks:
+        run_peaks()
         return
     import torch
     import bit_quantized_attention_amd as qa

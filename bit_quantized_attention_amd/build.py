@@ -3,7 +3,9 @@
     python -m bit_quantized_attention_amd.build
 
 Each source is compiled with hipcc to an object under ``_build/`` (in
-parallel), then linked into ``bit_quantized_attention_amd/libqattn.so``.
+parallel), then linked into ``bit_quantized_attention_amd/libqattn.so``. The
+benchmark's peak-rate micro-benchmarks (``csrc/peaks.hip``) go into a library
+of their own, ``libqattn_peaks.so``, which the attention path never loads.
 """
 
 from __future__ import annotations
@@ -18,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
+PEAKS_LIB = os.path.join(PKG, "libqattn_peaks.so")
 SOURCES = ["smooth_quant.hip", "block_mask.hip", "attn_fwd.hip", "head_error.hip", "lowbit_mask.hip",
            "stripes.hip",
            "api.cpp"]
@@ -42,18 +45,23 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = True, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + ["peaks.hip"]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS_LIB}")
     return LIB
 
 

@@ -195,19 +195,23 @@ void attn_fwd_kernel(FwdArgs a) {
   // landing in another, and waits only for the loads of the buffer it reads.
   // (Its tracking has room for few objects; one per stage keeps every read of
   // the loop clear of the loads in flight.)
-  static_assert(NBUF == 3 || NBUF == 4, "three or four staging buffers");
+  static_assert(NBUF >= 3 && NBUF <= 6, "three to six staging buffers");
   constexpr int KB = G::KBUF + 256;  // K tile plus the tail carrying its scale
   constexpr int SB = KB + G::VBUF;   // one stage
   __shared__ __attribute__((aligned(16))) int8_t stage0[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage1[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage2[SB];
   __shared__ __attribute__((aligned(16))) int8_t stage3[NBUF > 3 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) int8_t stage4[NBUF > 4 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) int8_t stage5[NBUF > 5 ? SB : 16];
   auto stage = [&](auto i) -> int8_t* {
     constexpr int j = decltype(i)::value % NBUF;
     if constexpr (j == 0) return stage0;
     else if constexpr (j == 1) return stage1;
     else if constexpr (j == 2) return stage2;
-    else return stage3;
+    else if constexpr (j == 3) return stage3;
+    else if constexpr (j == 4) return stage4;
+    else return stage5;
   };
   auto kbuf = [&](auto i) -> int8_t* { return stage(i); };
   auto vbuf = [&](auto i) -> int8_t* { return stage(i) + KB; };
@@ -613,7 +617,9 @@ void attn_fwd_kernel(FwdArgs a) {
   // With A = alpha * 1.5*2^23 split into A_hi + A_lo (exact), the fma
   // alpha*Sb - A_hi is alpha*S + A_lo, so the exponent alpha*S - m is
   // fma(alpha, Sb, -A_hi) - (m + A_lo): two roundings of numbers of the size
-  // of the exponent itself.
+  // of the exponent itself. (One fma against a rounded A + m would shift a
+  // tile's exponents by up to alpha/2, enough to flip the 16-bit rounding of
+  // many P.)
   // The reference m follows the rule of the module comment, but the row max
   // is only formed when some lane's partial sum exceeds kSumFilter: a move
   // needs an element more than kTau above m, i.e. a P above 2^kTau. Then the
@@ -636,7 +642,8 @@ void attn_fwd_kernel(FwdArgs a) {
       // the row max below), and its partial sum
       auto exps = [&](float m, float ahi, auto&& grp_hook) -> float {
         const float cm = m + a_lo;
-        float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // -0 is the additive identity, so the first additions fold away
+        float lsum[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
         static_for<0, 4>([&](auto gc) {
           constexpr int kb = decltype(gc)::value >> 1;
           constexpr int half = decltype(gc)::value & 1;
@@ -793,7 +800,7 @@ void attn_fwd_kernel(FwdArgs a) {
     const int lim = (row0 + l32) - (key0 + 4 * h);
     auto exps = [&](float m) -> float {
       const float cm = cq + m;
-      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float lsum[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         op_t pk;
@@ -906,7 +913,7 @@ void attn_fwd_kernel(FwdArgs a) {
         }
       }
     auto exps = [&](float m) -> float {
-      float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float lsum[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1027,16 +1034,41 @@ void attn_fwd_kernel(FwdArgs a) {
       // four groups of V(t-1) at once, each set shared by the QB blocks
       constexpr int NVS = QB == 1 ? 2 : 4;
       op_t vset[NVS][G::DB];
+      // QB = 1: the second 32-key block's INT8 products (kb = 1) run inside
+      // the first two softmax groups, which only read the first block's S:
+      // the matrix unit then has work while the softmax starts, instead of a
+      // phase of products with the vector unit idle
+      constexpr bool kSplitQK = QB == 1;
+      v4i kf1[G::KS];
       if (wave_live) {
         alpha = alpha_q * tile_kscale(kbuf(cur));
         static_for<0, NVS>([&](auto gc) { load_vgrp(vp, decltype(gc)::value, vset[decltype(gc)::value]); });
-        qk(kbuf(cur), s);
+        if constexpr (kSplitQK) {
+          const int8_t* kbp = kbuf(cur);
+#pragma unroll
+          for (int ks = 0; ks < G::KS; ++ks)
+            kf1[ks] = *reinterpret_cast<const v4i*>(kbp + 32 * G::KROW + k_frag_off[ks]);
+#pragma unroll
+          for (int ks = 0; ks < G::KS; ++ks) {
+            const v4i kf = *reinterpret_cast<const v4i*>(kbp + k_frag_off[ks]);
+            s[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[0][ks], ks == 0 ? sbias : s[0][0], 0, 0, 0);
+          }
+        } else {
+          qk(kbuf(cur), s);
+        }
       }
       issue(tl, tl_hs, kbuf(nxt), vbuf(nxt));
       if (wave_live) {
         auto lagged_pv = [&](auto qbc, auto gc) {
           constexpr int qb = decltype(qbc)::value;
           constexpr int g = decltype(gc)::value;
+          if constexpr (kSplitQK && g < 2) {
+            // k-steps [g*KS/2, (g+1)*KS/2) of the kb = 1 product
+#pragma unroll
+            for (int ks = g * G::KS / 2; ks < (g + 1) * G::KS / 2; ++ks)
+              s[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf1[ks], qf[0][ks], ks == 0 ? sbias : s[1][0],
+                                                              0, 0, 0);
+          }
           op_t (&vf)[G::DB] = vset[g % NVS];
 #pragma unroll
           for (int db = 0; db < G::DB; ++db)
