@@ -184,7 +184,10 @@ qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool,
  *      query block's causal range, and counts above max_keep are ignored.
  * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL. A query row with
  *      no visible key gets O = 0 and lse = -inf.
- * Errors: NULL; SHAPE/UNSUPPORTED; ALIGN; ARG when exactly one of
+ *      A block listed more than once is attended as often as it is listed
+ *      (its weight counts that many times in O and lse, as in the oracle).
+ * Errors: NULL; SHAPE/UNSUPPORTED, also UNSUPPORTED with a mask when
+ *      N > 131072 (N/64 > 2048 blocks); ALIGN; ARG when exactly one of
  *      kv_idx/kv_cnt is NULL, or with a mask when max_keep < 1 or
  *      max_keep > 2048; DEVICE.
  */

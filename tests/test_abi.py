@@ -188,6 +188,9 @@ def test_fwd_arguments(lib):
     assert _fw(p, idx=A) == ARG           # kv_idx without kv_cnt
     assert _fw(p, cnt=A) == ARG
     assert _fw(p, idx=A, cnt=A, mk=0) == ARG
+    # a kept list indexes at most 2048 blocks of 64 keys; dense has no such limit
+    assert _fw(_p(N=131072 + 128), idx=A, cnt=A, mk=16) == UNSUP
+    assert _fw(_p(N=(1 << 21) + 128), idx=A, cnt=A, mk=16) == UNSUP
 
 
 def test_fwd_promoted_arguments(lib):
