@@ -58,6 +58,9 @@ if ROOT not in sys.path:
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 matrix peak (TOPS)
 PEAK_BF16_TFLOPS = 2500.0     # dense FP16/BF16 matrix peak
 PEAK_HBM_GBS = 8000.0
+# half the attention's operations (Q K^T) at the INT8 peak, half (P V) at the
+# 16-bit peak
+BLENDED_PEAK_TOPS = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
 
 
 # file-name slugs of the workloads (profile summaries are named after them)
@@ -192,7 +195,64 @@ def parse():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--peaks", action="store_true",
                     help="only run the peak-rate micro-benchmarks (matrix, vector, LDS, HBM)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 64K (long-context causal) forward that the default 8K line "
+                         "reports beside its own")
     return ap.parse_args()
+
+
+def roofline_fracs(alg_ops: float, ms: float, traffic):
+    """The attention forward's rate against each bound: the INT8 matrix peak
+    (the metric's fraction), the 16-bit matrix peak for its P V half, the
+    blended matrix bound (half the operations at each peak) and, from the
+    counted bytes, the HBM peak."""
+    tops = alg_ops / (ms * 1e-3) / 1e12
+    out = {"frac_int8": tops / PEAK_INT8_TOPS,
+           "frac_fp16_pv_half": (tops / 2) / PEAK_BF16_TFLOPS,
+           "frac_blended": tops / BLENDED_PEAK_TOPS,
+           "hbm_frac": None if traffic is None else traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
+def measure_long_context(warmup: int = 1, steps: int = 3):
+    """The metric's second point: the 64K causal workload (B1 Hq32 Hkv8
+    N65536 d128 bf16), smoothing + quantization, then the dense forward timed
+    with events on its launch stream (outside the main timed region)."""
+    import torch
+    import bit_quantized_attention_amd as qa
+    from synthetic import make_config
+    p, t = make_config(4)
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
+    del t
+    plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    plan.smooth_quant(q, k)
+    for _ in range(warmup):
+        plan.fwd(v, o)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        plan.fwd(v, o)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    fwd = float(np.mean(ms))
+    alg = dense_algorithmic_ops(p)
+    literal = 4.0 * p.N * p.N * p.d * p.Hq * p.B
+    traffic = counted_traffic(4)
+    rec = {"workload": p.name, "N": p.N, "fwd_ms": fwd, "fwd_ms_min": float(np.min(ms)),
+           "steps": steps, "fwd_tops_literal": literal / (fwd * 1e-3) / 1e12,
+           "fwd_tops_algorithmic": alg / (fwd * 1e-3) / 1e12,
+           "literal_frac_int8": literal / (fwd * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+           "traffic": traffic}
+    rec.update(roofline_fracs(alg, fwd, traffic))
+    del q, k, v, o, plan
+    torch.cuda.empty_cache()
+    return rec
 
 
 def dense_algorithmic_ops(p) -> float:
@@ -476,6 +536,8 @@ def main():
     else:
         alg = dense_algorithmic_ops(p)
     achieved = alg / (fwd_avg * 1e-3) / 1e12
+    traffic = counted_traffic(args.config, "attn_fwd_stripes" if stripes else
+                              "attn_fwd_promoted" if args.promote else "attn_fwd")
     # Q: read 2 B + write 1 B per element; K: two reads of 2 B + write 1 B
     pre_bytes = (p.B * p.Hq * p.N * p.d * 3 + p.B * p.Hkv * p.N * p.d * 5)
     res = {
@@ -507,13 +569,14 @@ def main():
             "bound": "mfma",
             "achieved": achieved,
             "peak": peak,
-            "unit": "TFLOP/s",
+            # tera-operations per second: INT8 and 16-bit multiply-adds count 2
+            "unit": "TOP/s",
             "frac": achieved / peak,
-            "traffic": counted_traffic(args.config, "attn_fwd_stripes" if stripes else
-                                       "attn_fwd_promoted" if args.promote else "attn_fwd"),
+            "traffic": traffic,
             "kernel": "attn_fwd",
             "algorithmic_ops_per_launch": alg,
             "avg_launch_ms": fwd_avg,
+            **({} if (args.promote or adaptive) else roofline_fracs(alg, fwd_avg, traffic)),
         },
         "fwd_ms": fwd_avg,
         "fwd_tops_literal": literal / (fwd_avg * 1e-3) / 1e12,
@@ -524,8 +587,13 @@ def main():
         "fwd_ms_median": float(np.median(fwd_ms)),
         "smooth_quant_ms_cache_flushed": pre_flushed_ms,
         "smooth_quant_gbs_cache_flushed": pre_bytes / (pre_flushed_ms * 1e-3) / 1e9,
-        "blended_mfma_peak_tops": 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS),
+        "smooth_quant_hbm_frac_cache_flushed": pre_bytes / (pre_flushed_ms * 1e-3) / 1e9
+        / PEAK_HBM_GBS,
+        "blended_mfma_peak_tops": BLENDED_PEAK_TOPS,
     }
+    if (args.config == 2 and not (args.promote or adaptive or stripes) and not args.no_long):
+        # the metric is quoted at 8K and 64K: the 64K forward beside the 8K line
+        res["long_context"] = measure_long_context()
     if promote_info is not None:
         res["adaptive" if adaptive else "stripes" if stripes else "promote"] = promote_info
     if not args.no_cpu_baseline:

@@ -72,3 +72,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_roofline_fractions():
+    # 549.8 GOP (the 8K causal workload) in 0.5 ms: 1099.6 TOP/s
+    ops = 4.0 * 128 * 8192 * 8193 / 2 * 32
+    f = bench.roofline_fracs(ops, 0.5, 160e6)
+    tops = ops / 0.5e-3 / 1e12
+    assert abs(f["frac_int8"] - tops / 5000.0) < 1e-12
+    # half the operations (P V) at the 16-bit peak
+    assert abs(f["frac_fp16_pv_half"] - (tops / 2) / 2500.0) < 1e-12
+    # blended bound 1 / (0.5/5000 + 0.5/2500) = 3333.3 TOP/s
+    assert abs(bench.BLENDED_PEAK_TOPS - 10000.0 / 3.0) < 1e-9
+    assert abs(f["frac_blended"] - tops / (10000.0 / 3.0)) < 1e-12
+    assert abs(f["hbm_frac"] - 160e6 / 0.5e-3 / 8e12) < 1e-12
+    assert bench.roofline_fracs(ops, 0.5, None)["hbm_frac"] is None
