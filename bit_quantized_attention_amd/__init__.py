@@ -33,7 +33,11 @@ KV_TILE = 64
 SOFTMAX_REF_THRESHOLD = 8
 
 _STATUS = {0: "QATTN_OK", 1: "QATTN_ERR_NULL", 2: "QATTN_ERR_SHAPE", 3: "QATTN_ERR_ALIGN",
-           4: "QATTN_ERR_UNSUPPORTED", 5: "QATTN_ERR_ARG", 6: "QATTN_ERR_DEVICE"}
+           4: "QATTN_ERR_UNSUPPORTED", 5: "QATTN_ERR_ARG", 6: "QATTN_ERR_DEVICE",
+           7: "QATTN_ERR_SCRATCH"}
+# size of the allocation-free smoothing entry point's static scratch
+# (QATTN_NOALLOC_SCRATCH_BYTES in include/qattn.h)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -71,6 +75,8 @@ def load(path: str = LIB_PATH):
     lib.qattn_max_keep.restype = i32
     lib.qattn_smooth_quant.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.qattn_smooth_quant.restype = ctypes.c_int
+    lib.qattn_smooth_quant_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.qattn_smooth_quant_noalloc.restype = ctypes.c_int
     lib.qattn_block_mask.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.qattn_block_mask.restype = ctypes.c_int
     lib.qattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -166,6 +172,16 @@ def qattn_smooth_quant(p, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_
                                    _stream(stream))
     if check:
         _check(st, "qattn_smooth_quant")
+    return st
+
+
+def qattn_smooth_quant_noalloc(p, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool,
+                               stream=None, check=True) -> int:
+    st = load().qattn_smooth_quant_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(q_i8),
+                                           _ptr(q_scale), _ptr(k_i8), _ptr(k_scale), _ptr(k_mean),
+                                           _ptr(q_pool), _ptr(k_pool), _stream(stream))
+    if check:
+        _check(st, "qattn_smooth_quant_noalloc")
     return st
 
 

@@ -69,6 +69,8 @@ const char* qattn_status_str(qattn_status_t status) {
       return "unsupported problem (d must be 64 or 128, N a multiple of 128, dtype f16/bf16)";
     case QATTN_ERR_ARG: return "invalid argument (flag, keep ratio, max_keep or workspace size)";
     case QATTN_ERR_DEVICE: return "HIP launch failed";
+    case QATTN_ERR_SCRATCH:
+      return "the problem needs more scratch than the allocation-free entry point's static array";
   }
   return "unknown status";
 }
@@ -103,6 +105,23 @@ qattn_status_t qattn_smooth_quant(const qattn_problem_t* p, const void* q, const
   return launched(qattn::launch_smooth_quant(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool,
                                              k_pool, workspace,
                                              static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_smooth_quant_noalloc(const qattn_problem_t* p, const void* q, const void* k,
+                                          int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                                          float* k_scale, float* k_mean, float* q_pool,
+                                          float* k_pool, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (!q || !k || !q_i8 || !q_scale || !k_i8 || !k_scale || !k_mean) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (qattn::ksum_workspace_bytes(s) > qattn::kNoallocScratchBytes) return QATTN_ERR_SCRATCH;
+  return launched(qattn::launch_smooth_quant_noalloc(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean,
+                                                     q_pool, k_pool,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 qattn_status_t qattn_block_mask(const qattn_problem_t* p, const float* q_pool, const float* k_pool,

@@ -30,6 +30,17 @@ hipError_t launch_smooth_quant(const Shape& s, const void* q, const void* k, int
                                float* q_pool, float* k_pool, void* workspace,
                                hipStream_t stream);
 
+// Size of the static device scratch of the allocation-free smoothing entry
+// point (one array per GPU, held until the process ends).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+
+// launch_smooth_quant with its partial sums in that static scratch of the
+// current device (its address looked up once per device, never allocated).
+hipError_t launch_smooth_quant_noalloc(const Shape& s, const void* q, const void* k, int8_t* q_i8,
+                                       float* q_scale, int8_t* k_i8, float* k_scale,
+                                       float* k_mean, float* q_pool, float* k_pool,
+                                       hipStream_t stream);
+
 // Bytes of pooled-vector INT8 codes and scales that launch_block_mask needs.
 size_t mask_workspace_bytes(const Shape& s);
 // Largest N/64 the block mask supports.

@@ -13,6 +13,8 @@
 #include "device_util.h"
 #include "qattn_internal.h"
 
+#include <mutex>
+
 // The rounding sequence of every value here is fixed by the definition: no
 // contraction of a*b+c into fma anywhere in this file.
 #pragma clang fp contract(off)
@@ -257,7 +259,49 @@ hipError_t launch(const Shape& s, const void* q, const void* k, int8_t* q_i8, fl
   return hipGetLastError();
 }
 
+// The allocation-free entry point's partial sums: a file-scope device array,
+// one copy per GPU. Host code never passes its name to a kernel (on the host
+// the name is a stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress below.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The scratch address of the current device, looked up on the device's first
+// call (with the device current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_smooth_quant_noalloc(const Shape& s, const void* q, const void* k, int8_t* q_i8,
+                                       float* q_scale, int8_t* k_i8, float* k_scale,
+                                       float* k_mean, float* q_pool, float* k_pool,
+                                       hipStream_t stream) {
+  if (ksum_workspace_bytes(s) > kNoallocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // every partial sum is written by the first launch before the second reads
+  // it, so nothing needs clearing
+  return launch_smooth_quant(s, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_pool, k_pool, ws,
+                             stream);
+}
 
 hipError_t launch_smooth_quant(const Shape& s, const void* q, const void* k, int8_t* q_i8,
                                float* q_scale, int8_t* k_i8, float* k_scale, float* k_mean,

@@ -49,7 +49,8 @@ typedef enum {
   QATTN_ERR_ALIGN = 3,       /* a tensor pointer is not 16-byte aligned     */
   QATTN_ERR_UNSUPPORTED = 4, /* d not 64/128, N % 128 != 0, unknown dtype   */
   QATTN_ERR_ARG = 5,         /* bad flag, keep ratio, max_keep or workspace */
-  QATTN_ERR_DEVICE = 6       /* a HIP launch reported an error              */
+  QATTN_ERR_DEVICE = 6,      /* a HIP launch reported an error              */
+  QATTN_ERR_SCRATCH = 7      /* beyond the allocation-free entry point's static scratch */
 } qattn_status_t;
 
 typedef enum { QATTN_F16 = 0, QATTN_BF16 = 1 } qattn_dtype_t;
@@ -124,6 +125,31 @@ qattn_status_t qattn_smooth_quant(const qattn_problem_t* p, const void* q, const
                                   float* k_scale, float* k_mean, float* q_pool,
                                   float* k_pool, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * qattn_smooth_quant_noalloc -- qattn_smooth_quant without a workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * kernels and results as qattn_smooth_quant (bit for bit); the exact
+ * partial K sums live in a static device array of QATTN_NOALLOC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends (its address
+ * is looked up on the device's first call). No hipMalloc, hipFree or other
+ * allocation happens in this call.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (two streams, two threads) race and corrupt each other's k_mean. Every
+ * partial sum is written before it is read, so nothing needs clearing between
+ * calls.
+ * Arguments, layouts and outputs as qattn_smooth_quant.
+ * Errors: NULL; SHAPE/UNSUPPORTED; ALIGN; SCRATCH when the partial sums,
+ *      B * Hkv * ceil(N/128) * d * 16 bytes, exceed the array (for example
+ *      B = 1, Hkv = 8, d = 128 fits up to N = 131072); DEVICE.
+ */
+#define QATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+qattn_status_t qattn_smooth_quant_noalloc(const qattn_problem_t* p, const void* q, const void* k,
+                                          int8_t* q_i8, float* q_scale, int8_t* k_i8,
+                                          float* k_scale, float* k_mean, float* q_pool,
+                                          float* k_pool, void* stream);
 
 /*
  * qattn_block_mask -- per query block, the key blocks to keep.

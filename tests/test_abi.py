@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert len(qa.qattn_status_str(s)) > 0
     assert qa.qattn_status_str(99) == "unknown status"
     assert "gfx950" in qa.qattn_version()
@@ -131,7 +131,16 @@ def _fs(p, **over):
                                 stream=0, check=False)
 
 
-@pytest.mark.parametrize("call", [_sq, _bm, _fw, _fp, _he, _fa, _lb, _ss, _fs])
+def _sn(p, **over):
+    args = dict(q=A, k=A, q_i8=A, q_scale=A, k_i8=A, k_scale=A, k_mean=A, q_pool=None,
+                k_pool=None)
+    args.update(over)
+    return qa.qattn_smooth_quant_noalloc(p, args["q"], args["k"], args["q_i8"], args["q_scale"],
+                                         args["k_i8"], args["k_scale"], args["k_mean"],
+                                         args["q_pool"], args["k_pool"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("call", [_sq, _sn, _bm, _fw, _fp, _he, _fa, _lb, _ss, _fs])
 def test_problem_validation(lib, call):
     assert call(_p(B=0)) == SHAPE
     assert call(_p(Hq=0)) == SHAPE
@@ -162,6 +171,20 @@ def test_smooth_quant_arguments(lib):
     need = qa.qattn_workspace_bytes(p)
     assert need > 0
     assert _sq(p, workspace_bytes=need - 1) == ARG
+
+
+def test_smooth_quant_noalloc_arguments(lib):
+    p = _p()
+    for name in ["q", "k", "q_i8", "q_scale", "k_i8", "k_scale", "k_mean"]:
+        assert _sn(p, **{name: None}) == NULL, name
+        assert _sn(p, **{name: A + 8}) == ALIGN, name
+    assert _sn(p, q_pool=A + 4) == ALIGN
+    # partial sums of B * Hkv * ceil(N/128) * d * 16 bytes must fit the static
+    # 16 MiB array: here 2 * 4097 * 128 * 16 bytes do not
+    need = 2 * ((524288 + 128) // 128) * 128 * 16
+    assert need > qa.NOALLOC_SCRATCH_BYTES
+    assert _sn(_p(N=524288 + 128)) == 7  # QATTN_ERR_SCRATCH
+    assert "scratch" in qa.qattn_status_str(7)
 
 
 def test_block_mask_arguments(lib):
@@ -299,3 +322,5 @@ def test_binding_constants_match_the_header():
     assert int(defs["QATTN_K_BLOCK"]) == qa.K_BLOCK
     assert int(defs["QATTN_KV_TILE"]) == qa.KV_TILE
     assert int(defs["QATTN_SOFTMAX_REF_THRESHOLD"]) == qa.SOFTMAX_REF_THRESHOLD
+    assert "#define QATTN_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
+    assert qa.NOALLOC_SCRATCH_BYTES == 16 << 20
