@@ -125,6 +125,8 @@ PEAK_KINDS = [
     (0, 0, "mfma_i8_32x32x32", "TOPS", 1e12),
     (1, 0, "mfma_bf16_32x32x16", "TFLOP/s", 1e12),
     (2, 0, "mfma_mix_1i8_2bf16", "TOPS", 1e12),
+    (14, 0, "mfma_fp4_32x32x64", "TOPS", 1e12),
+    (15, 0, "mfma_fp4_32x32x64_vgpr_scales", "TOPS", 1e12),
     (3, 0, "valu_fma_f32", "G lane-instr/s", 1e9),
     (4, 0, "valu_exp_f32", "G lane-instr/s", 1e9),
     *[(5, n, f"coissue_bf16_mfma_plus_{n}_exp_1wave_per_simd", "TFLOP/s", 1e12)

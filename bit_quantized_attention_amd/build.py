@@ -36,9 +36,16 @@ CFLAGS = [
 ]
 
 
+# per-source flags: the 4-bit score kernel keeps its matrix results in ordinary
+# VGPRs (the compiler's default puts them in AGPRs, and every estimate then
+# costs a v_accvgpr_read before its max)
+FILE_FLAGS = {"lowbit_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), *extra, "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -113,6 +113,27 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const uint16_t* __rest
   if ((sub & 3) == 0) (isq ? L.qe : L.ke)[r * (D / kMx) + sub / 4] = (uint8_t)(E + 127);
 }
 
+// Max over the 64 lanes without LDS round trips (a shuffle chain waits for
+// each of its six LDS permutes): DPP butterflies within each row of 16 lanes
+// (xor 1 and xor 2 by quad permutes, then the half-row and row mirrors), then
+// the row broadcasts of lanes 15 and 31 fold the four rows upward. Lane 63
+// ends with the maximum over all lanes.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int x = __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK,
+                                            0xF, false);
+  return __builtin_fmaxf(v, __int_as_float(x));
+}
+__device__ __forceinline__ float wave_max_to_lane63(float v) {
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max<0x140, 0xF>(v);  // row_mirror: every lane holds its row's max
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 struct ScoreArgs {
   LowbitLayout L;
   int B, Hq, Hkv, group, N, nqb, nkb, causal;
@@ -154,42 +175,60 @@ __global__ __launch_bounds__(256) void lowbit_score_kernel(ScoreArgs a) {
       }
     }
     float* out = a.L.scores + (bhq * a.nqb + i) * a.nkb;
+    // Key block j's A-operand fragments (key 64 j + 32 kb + l32, channels
+    // 64 ks + 32 h + [0, 32)) and their E8M0 scales; the loop loads block
+    // j + 1 while it scores block j.
+    struct KFrag {
+      v8i f[2][KS];
+      int e[2][KS];
+    };
+    auto load_kblock = [&](int j, KFrag& kf) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const size_t kr = krow0 + kKBlock * j + 32 * kb + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 w = *reinterpret_cast<const uint4*>(a.L.k4 + kr * (D / 2) + 32 * ks + 16 * h);
+          kf.f[kb][ks] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+          kf.e[kb][ks] = a.L.ke[kr * (D / kMx) + 2 * ks + h];
+        }
+      }
+    };
     // Per key block: the masked (diagonal) blocks take the element test, the
     // others none; four running maxima per lane keep the max chains short.
-    auto score_block = [&](int j, auto diag_c) {
+    auto score_block = [&](int j, const KFrag& kf, auto diag_c) {
       constexpr bool DIAG = decltype(diag_c)::value;
       float best[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // A operand: key 64 j + 32 kb + l32
-        const size_t kr = krow0 + kKBlock * j + 32 * kb + l32;
-        v8i kf[KS];
-        int kscl[KS];
+        // two 32-row blocks at a time, their k-steps interleaved, so that no
+        // matrix instruction waits for the one just before it
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 w = *reinterpret_cast<const uint4*>(a.L.k4 + kr * (D / 2) + 32 * ks + 16 * h);
-          kf[ks] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-          kscl[ks] = a.L.ke[kr * (D / kMx) + 2 * ks + h];
-        }
+        for (int rp = 0; rp < RB; rp += 2) {
+          v16f s[2];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          v16f s;
+          for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+            for (int r = 0; r < 16; ++r) s[u][r] = 0.0f;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[ks], qf[rb][ks], s, 4, 4, 0,
-                                                                 kscl[ks], 0, qs[rb][ks]);
-          // element r: key 64 j + 32 kb + 8 (r/4) + 4 h + r%4, query 128 i + 32 rb + l32
-          const int lim = (32 * rb + l32) + kQBlock * i - (kKBlock * j + 32 * kb + 4 * h);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float v = s[r];
-            if constexpr (DIAG) {
-              const int off = 8 * (r >> 2) + (r & 3);
-              v = off > lim ? -__builtin_inff() : v;
+            for (int u = 0; u < 2; ++u)
+              s[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  kf.f[kb][ks], qf[rp + u][ks], s[u], 4, 4, 0, kf.e[kb][ks], 0, qs[rp + u][ks]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            // element r: key 64 j + 32 kb + 8 (r/4) + 4 h + r%4, query 128 i + 32 (rp+u) + l32
+            const int lim = (32 * (rp + u) + l32) + kQBlock * i - (kKBlock * j + 32 * kb + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float v = s[u][r];
+              if constexpr (DIAG) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                v = off > lim ? -__builtin_inff() : v;
+              }
+              best[r & 3] = __builtin_fmaxf(best[r & 3], v);
             }
-            best[r & 3] = __builtin_fmaxf(best[r & 3], v);
           }
         }
       }
@@ -197,11 +236,22 @@ __global__ __launch_bounds__(256) void lowbit_score_kernel(ScoreArgs a) {
     };
     // the last key blocks of a causal query block need the element test
     const int nplain = a.causal ? min(nvalid, (kQBlock * i + 1) / kKBlock) : nvalid;
-    for (int j = 0; j < nvalid; ++j) {
-      float best = j < nplain ? score_block(j, std::integral_constant<bool, false>{})
-                              : score_block(j, std::integral_constant<bool, true>{});
-      best = wave_max(best);
-      if (lane == 0) out[j] = best;
+    auto finish = [&](int j, const KFrag& kf) {
+      float best = j < nplain ? score_block(j, kf, std::integral_constant<bool, false>{})
+                              : score_block(j, kf, std::integral_constant<bool, true>{});
+      best = wave_max_to_lane63(best);
+      if (lane == 63) out[j] = best;
+    };
+    // The prefetches are unconditional (clamped to the last block, whose
+    // extra load is harmless): with a fixed number of loads in flight the
+    // compiler waits only for the older block's loads, not for every load.
+    KFrag ka, kb2;
+    load_kblock(0, ka);
+    for (int j = 0; j < nvalid; j += 2) {
+      load_kblock(min(j + 1, nvalid - 1), kb2);
+      finish(j, ka);
+      load_kblock(min(j + 2, nvalid - 1), ka);
+      if (j + 1 < nvalid) finish(j + 1, kb2);
     }
   }
 }

@@ -38,6 +38,8 @@ enum Kind {
   kSplitFma = 12,   // two waves per SIMD: one issues BF16 matrix instructions only, the
                     // other `param` v_fma_f32 per matrix instruction of its partner
   kSplitExp = 13,   // the same with v_exp_f32
+  kMfmaFp4 = 14,    // v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands, 8 accumulators
+  kMfmaFp4Vs = 15,  // the same with per-lane E8M0 scales in VGPRs
 };
 
 struct Clock {
@@ -229,6 +231,40 @@ __global__ __launch_bounds__(256) void k_coissue(int iters, unsigned long long* 
 #pragma unroll
   for (int j = 0; j < 16; ++j) s += x[j];
   if (s == 1.2345f) sink[0] = (int)lds_pad[threadIdx.x];
+}
+
+template <bool VSCALE>
+__global__ __launch_bounds__(256) void k_mfma_fp4(int iters, unsigned long long* clk, int* sink) {
+  typedef int v8i __attribute__((ext_vector_type(8)));
+  const v8i a = {(int)threadIdx.x, 0x11111111, 0x22222222, 0x01234567, 0, 0, 0, 0};
+  const v8i b = {0x76543210, (int)threadIdx.x, 0x13572468, 0x24681357, 0, 0, 0, 0};
+  v16f c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[j][r] = (float)(j + r);
+  const Clock ck = clock_start();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+    {
+      if constexpr (VSCALE) {
+        int sa = 126 + (int)(threadIdx.x & 1), sb = 127 - (int)((threadIdx.x >> 1) & 1);
+        keep(sa);
+        keep(sb);
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 4, 4, 0, sa, 0, sb);
+      } else {
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], 4, 4, 0, 127, 0, 127);
+      }
+    }
+  }
+  clock_stop(ck, clk);
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[j][r];
+  if (s == 1.2345f) sink[0] = 1;
 }
 
 // One wave per SIMD: per iteration 8 16x16x32 BF16 matrix instructions (16
@@ -535,6 +571,16 @@ extern "C" int qattn_peak(int kind, int param, double* result) {
 #undef QP_SP
         break;
       }
+      case kMfmaFp4:
+        iters = 20000;
+        per_iter = 4.0 * 8 * 131072.0;
+        hipLaunchKernelGGL(k_mfma_fp4<false>, dim3(blocks), dim3(256), 0, 0, iters, clk, sink);
+        break;
+      case kMfmaFp4Vs:
+        iters = 20000;
+        per_iter = 4.0 * 8 * 131072.0;
+        hipLaunchKernelGGL(k_mfma_fp4<true>, dim3(blocks), dim3(256), 0, 0, iters, clk, sink);
+        break;
       case kLdsB128:
         iters = 20000;
         per_iter = 256.0 * 8 * 16;
