@@ -19,6 +19,9 @@ written for reading, not for speed:
 * ``emulate_promoted_attention`` / ``promote_plan`` -- promote instead of
   skip: the kept blocks at 16-bit Q K^T, every other visible block through
   the INT8 path, merged by the same online softmax.
+* ``emulate_promoted_fp4_attention`` (module ``promote_fp4``) -- promote
+  instead of skip with an MX FP4 low path: the kept blocks at 16-bit Q K^T,
+  every other visible block at 4-bit Q K^T, the same online softmax.
 * ``lowbit_block_mask`` (module ``lowbit``) -- the element-level 4-bit
   block estimator: MX FP4 Q and smoothed K, the block score as the largest
   estimated product over the block's visible pairs, the same selection rule.
@@ -62,3 +65,4 @@ from .attention import (exact_attention, emulate_attention, emulate_promoted_att
                         adaptive_lists)
 from .lowbit import lowbit_block_mask, lowbit_scores, mxfp4_quantize  # noqa: F401,E402
 from .stripes import stripe_select, emulate_stripe_attention  # noqa: F401,E402
+from .promote_fp4 import emulate_promoted_fp4_attention  # noqa: F401,E402
