@@ -1,7 +1,8 @@
 """Benchmark of the quantized attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
-                    [--promote | --adaptive TAU | --stripes THETA] [--mask pooled|lowbit]
+                    [--promote [--low4] | --adaptive TAU | --stripes THETA]
+                    [--mask pooled|lowbit]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -23,6 +24,9 @@ mask keeps (the workload's keep ratio, else first + diagonal + top 10 %) run at
 algorithmic operations are those of the dense problem (4*d per visible pair),
 of which 2*d per promoted pair and 2*d per pair for P V are 16-bit; the peak
 is the matrix bound of that mix (INT8 and 16-bit work each at its own peak).
+With ``--low4`` as well the call is qattn_fwd_promoted_fp4: the other blocks
+take MX FP4 Q K^T (2*d per pair at the FP4 peak) instead of INT8, and the
+attention launch time includes the call's MX FP4 quantization of Q and K.
 
 With ``--mask lowbit`` the kept lists come from qattn_block_mask_lowbit (the
 element-level 4-bit estimator) instead of qattn_block_mask (pooled block
@@ -57,6 +61,7 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 matrix peak (TOPS)
 PEAK_BF16_TFLOPS = 2500.0     # dense FP16/BF16 matrix peak
+PEAK_FP4_TFLOPS = 10100.0     # dense FP4 (MX) matrix peak
 PEAK_HBM_GBS = 8000.0
 # half the attention's operations (Q K^T) at the INT8 peak, half (P V) at the
 # 16-bit peak
@@ -183,6 +188,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--promote", action="store_true",
                     help="promote the kept blocks to 16-bit Q K^T instead of skipping the rest")
+    ap.add_argument("--low4", action="store_true",
+                    help="with --promote: the blocks not promoted at MX FP4 Q K^T instead of INT8")
     ap.add_argument("--mask", choices=["pooled", "lowbit"], default="pooled",
                     help="block scores from pooled block means or element-level 4-bit estimates")
     ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
@@ -296,7 +303,7 @@ def stripe_pairs(key_idx: np.ndarray, key_cnt: np.ndarray, causal: bool) -> floa
 
 
 def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None,
-                     mask: str = "pooled", stripes=None):
+                     mask: str = "pooled", stripes=None, low4: bool = False):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -341,6 +348,9 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
                 oracle.emulate_stripe_attention(sq["q_i8"][:, n:n + 1], sq["q_scale"][:, n:n + 1],
                                                 sq["k_i8"], sq["k_scale"], v, p.causal, 1, 1,
                                                 sidx, scnt)
+            elif low4:
+                oracle.emulate_promoted_fp4_attention(q, k, sq["k_mean"], v, p.causal, len(hqs),
+                                                      1, idx, cnt, blocks=blocks)
             elif promote or adaptive is not None:
                 oracle.emulate_promoted_attention(sq["q_i8"], sq["q_scale"], sq["k_i8"],
                                                   sq["k_scale"], q, k, sq["k_mean"], v, p.causal,
@@ -370,7 +380,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         "sample": f"oracle smooth_quant + "
                   f"{('lowbit_block_mask + ' if mask == 'lowbit' else 'block_mask + ') if sparse else ''}"
                   f"{'head_error + ' if adaptive is not None else ''}"
-                  f"{'stripe_select + emulate_stripe_attention' if stripes is not None else ('emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention')} "
+                  f"{'stripe_select + emulate_stripe_attention' if stripes is not None else ('emulate_promoted_fp4_attention' if low4 else 'emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention')} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
                   f"({el:.1f} s); numpy BLAS {blas}",
     }
@@ -399,6 +409,8 @@ def main():
     q, k, v = (t[x].to(dev) for x in "qkv")
     if sum([args.promote, args.adaptive is not None, args.stripes is not None]) > 1:
         raise SystemExit("--promote, --adaptive and --stripes are exclusive")
+    if args.low4 and not args.promote:
+        raise SystemExit("--low4 is the low path of --promote")
     adaptive = args.adaptive is not None
     stripes = args.stripes is not None
     if adaptive or stripes:
@@ -406,7 +418,8 @@ def main():
     else:
         keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
-                   sparse=keep, promote=args.promote, pools=True if stripes else None)
+                   sparse=keep, promote=args.promote, low4=args.low4,
+                   pools=True if stripes else None)
     o = torch.empty_like(q)
     head_err = torch.empty((p.B, p.Hq), dtype=torch.float32, device=dev)
     head_hi = torch.empty((p.B, p.Hq), dtype=torch.int32, device=dev)
@@ -437,6 +450,8 @@ def main():
         if stripes:
             qa.qattn_fwd_stripes(plan.p, plan.q_i8, plan.q_scale, plan.k_i8, plan.k_scale, v,
                                  key_idx, key_cnt, args.stripe_keys, o, plan.lse)
+        elif args.low4:
+            plan.fwd_promoted_fp4(q, k, v, o)
         elif args.promote:
             plan.fwd_promoted(q, k, v, o)
         elif adaptive:
@@ -514,10 +529,13 @@ def main():
             prom = sparse_pairs(plan.kv_idx.cpu().numpy(), plan.kv_cnt.cpu().numpy(), p.causal)
         ops_16 = alg / 2 + 2.0 * p.d * prom
         ops_i8 = alg - ops_16
-        peak = alg / (ops_i8 / PEAK_INT8_TOPS + ops_16 / PEAK_BF16_TFLOPS)
+        low_peak = PEAK_FP4_TFLOPS if args.low4 else PEAK_INT8_TOPS
+        peak = alg / (ops_i8 / low_peak + ops_16 / PEAK_BF16_TFLOPS)
         promote_info = {"keep": list(keep) if keep else None,
                         "promoted_pair_fraction": prom / (alg / (4.0 * p.d)),
-                        "ops_int8_per_launch": ops_i8, "ops_16bit_per_launch": ops_16}
+                        "low_path": "mxfp4" if args.low4 else "int8",
+                        ("ops_fp4_per_launch" if args.low4 else "ops_int8_per_launch"): ops_i8,
+                        "ops_16bit_per_launch": ops_16}
         if adaptive:
             he = head_err.cpu().numpy()
             promote_info.update({"threshold": args.adaptive, "heads_16bit": int(head_hi.sum()),
@@ -539,6 +557,7 @@ def main():
         alg = dense_algorithmic_ops(p)
     achieved = alg / (fwd_avg * 1e-3) / 1e12
     traffic = counted_traffic(args.config, "attn_fwd_stripes" if stripes else
+                              "attn_fwd_promoted_fp4" if args.low4 else
                               "attn_fwd_promoted" if args.promote else "attn_fwd")
     # Q: read 2 B + write 1 B per element; K: two reads of 2 B + write 1 B
     pre_bytes = (p.B * p.Hq * p.N * p.d * 3 + p.B * p.Hkv * p.N * p.d * 5)
@@ -555,7 +574,8 @@ def main():
         "vs_baseline": None,
         "dtype": "i8+bf16" if p.dtype == "bf16" else "i8+f16",
         "data": "synthetic (seeded Gaussian Q/K/V with per-channel K offsets and outlier channels)",
-        "config": {"workload": p.name + (" (kept blocks promoted to 16-bit QK^T, the rest INT8)"
+        "config": {"workload": p.name + (" (kept blocks promoted to 16-bit QK^T, the rest "
+                                         f"{'MX FP4' if args.low4 else 'INT8'})"
                                          if args.promote else "") +
                    (f" (per-head precision, error threshold {args.adaptive})" if adaptive else "") +
                    (f" (anchor stripes, threshold {args.stripes}, up to {args.stripe_keys} keys)"
@@ -564,6 +584,7 @@ def main():
                    "causal": p.causal,
                    "sparse": None if (args.promote or adaptive or stripes) else p.sparse,
                    "promote": list(keep) if args.promote else None,
+                   "low_path": ("mxfp4" if args.low4 else "int8") if args.promote else None,
                    "adaptive_threshold": args.adaptive,
                    "stripes": [args.stripes, args.stripe_keys] if stripes else None,
                    "mask": args.mask if keep is not None else None, "input_dtype": p.dtype},
@@ -601,7 +622,8 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote,
                                                args.adaptive, args.mask,
-                                               (args.stripes, args.stripe_keys) if stripes else None)
+                                               (args.stripes, args.stripe_keys) if stripes else None,
+                                               low4=args.low4)
     print(json.dumps(res))
 
 

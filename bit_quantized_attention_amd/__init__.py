@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.qattn_smooth_quant.restype = ctypes.c_int
     lib.qattn_smooth_quant_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.qattn_smooth_quant_noalloc.restype = ctypes.c_int
+    lib.qattn_fwd_promoted_fp4.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.qattn_fwd_promoted_fp4.restype = ctypes.c_int
     lib.qattn_block_mask.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
     lib.qattn_block_mask.restype = ctypes.c_int
     lib.qattn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -185,6 +187,18 @@ def qattn_smooth_quant_noalloc(p, q, k, q_i8, q_scale, k_i8, k_scale, k_mean, q_
     return st
 
 
+def qattn_fwd_promoted_fp4(p, q, k, k_mean, v, kv_idx, kv_cnt, max_keep, o, lse, workspace,
+                           workspace_bytes=None, stream=None, check=True) -> int:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = load().qattn_fwd_promoted_fp4(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_mean), _ptr(v),
+                                       _ptr(kv_idx), _ptr(kv_cnt), max_keep, _ptr(o), _ptr(lse),
+                                       _ptr(workspace), workspace_bytes, _stream(stream))
+    if check:
+        _check(st, "qattn_fwd_promoted_fp4")
+    return st
+
+
 def qattn_block_mask(p, q_pool, k_pool, keep_num, keep_den, max_keep, kv_idx, kv_cnt,
                      workspace, workspace_bytes=None, stream=None, check=True) -> int:
     if workspace_bytes is None:
@@ -284,7 +298,8 @@ class Plan:
 
     ``sparse`` is None (dense) or a keep ratio (keep_num, keep_den). With
     ``promote`` the kept blocks are computed at 16-bit Q K^T and every other
-    block through the INT8 path, instead of being skipped.
+    block through the INT8 path, instead of being skipped; ``low4`` (with
+    ``promote``) takes those other blocks at MX FP4 Q K^T instead of INT8.
     """
 
     p: qattn_problem_t
@@ -293,11 +308,14 @@ class Plan:
     with_lse: bool = False
     pools: Optional[bool] = None  # pooled block means; default: only when sparse
     promote: bool = False
+    low4: bool = False
 
     def __post_init__(self):
         import torch
         if self.promote and self.sparse is None:
             raise ValueError("promote needs a keep ratio (the blocks to promote)")
+        if self.low4 and not self.promote:
+            raise ValueError("low4 is the low path of promote")
         p, dev = self.p, self.device
         B, Hq, Hkv, N, d = p.B, p.Hq, p.Hkv, p.N, p.d
         nqb, nkb = N // Q_BLOCK, N // K_BLOCK
@@ -323,6 +341,10 @@ class Plan:
             self.kv_idx = torch.empty((B, Hq, nqb, self.max_keep), dtype=torch.int32, **e)
             self.kv_cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, **e)
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, **e) if self.with_lse else None
+        self.workspace4 = None
+        if self.low4:
+            self.workspace4 = torch.empty(max(16, qattn_lowbit_workspace_bytes(p)),
+                                          dtype=torch.uint8, **e)
 
     def smooth_quant(self, q, k, stream=None):
         qattn_smooth_quant(self.p, q, k, self.q_i8, self.q_scale, self.k_i8, self.k_scale,
@@ -342,12 +364,18 @@ class Plan:
                            self.k_mean, v, self.kv_idx, self.kv_cnt, self.max_keep, o, self.lse,
                            stream=stream)
 
+    def fwd_promoted_fp4(self, q, k, v, o, stream=None):
+        qattn_fwd_promoted_fp4(self.p, q, k, self.k_mean, v, self.kv_idx, self.kv_cnt,
+                               self.max_keep, o, self.lse, self.workspace4, stream=stream)
+
     def run(self, q, k, v, o, stream=None):
         """The whole path: smooth + quantize, [block mask], attention."""
         self.smooth_quant(q, k, stream)
         if self.sparse is not None:
             self.block_mask(stream)
-        if self.promote:
+        if self.low4:
+            self.fwd_promoted_fp4(q, k, v, o, stream)
+        elif self.promote:
             self.fwd_promoted(q, k, v, o, stream)
         else:
             self.fwd(v, o, stream)
@@ -355,19 +383,21 @@ class Plan:
 
 
 def attention(q, k, v, causal: bool = False, sparse: Optional[Tuple[int, int]] = None,
-              return_plan: bool = False, with_lse: bool = False, promote: bool = False):
+              return_plan: bool = False, with_lse: bool = False, promote: bool = False,
+              low4: bool = False):
     """O = attention(Q, K, V) through the quantized path; Q [B,Hq,N,d], K/V [B,Hkv,N,d].
 
     ``sparse`` = (keep_num, keep_den) keeps the first, diagonal and top blocks
     per query block and skips the rest; with ``promote`` those blocks run at
-    16-bit Q K^T and the rest through the INT8 path instead.
+    16-bit Q K^T and the rest through the INT8 path instead (``low4``: at MX
+    FP4 Q K^T).
     """
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors")
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share one dtype")
-    plan = Plan(problem_of(q, k, causal), q.device, sparse, with_lse, promote=promote)
+    plan = Plan(problem_of(q, k, causal), q.device, sparse, with_lse, promote=promote, low4=low4)
     o = torch.empty_like(q)
     plan.run(q, k, v, o)
     return (o, plan) if return_plan else o

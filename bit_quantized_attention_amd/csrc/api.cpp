@@ -185,6 +185,29 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
                                          static_cast<hipStream_t>(stream)));
 }
 
+qattn_status_t qattn_fwd_promoted_fp4(const qattn_problem_t* p, const void* q, const void* k,
+                                      const float* k_mean, const void* v, const int32_t* kv_idx,
+                                      const int32_t* kv_cnt, int32_t max_keep, void* o, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.nkb() > qattn::fwd_max_sparse_tiles()) return QATTN_ERR_UNSUPPORTED;
+  if (!q || !k || !k_mean || !v || !kv_idx || !kv_cnt || !o || !workspace) return QATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, k_mean, v, kv_idx, kv_cnt, o, lse, workspace};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (max_keep < 1 || max_keep > qattn::fwd_max_sparse_tiles()) return QATTN_ERR_ARG;
+  if (workspace_bytes < qattn::lowbit_workspace_bytes(s, false)) return QATTN_ERR_ARG;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = qattn::launch_mxfp4_quant(s, q, k, k_mean, workspace, hs);
+  if (e != hipSuccess) return QATTN_ERR_DEVICE;
+  const qattn::Fp4Codes codes = qattn::fp4_codes(workspace, s);
+  return launched(qattn::launch_attn_fwd(s, nullptr, nullptr, nullptr, nullptr, v, kv_idx, kv_cnt,
+                                         max_keep, q, k, k_mean, nullptr, false, o, lse, hs,
+                                         &codes));
+}
+
 size_t qattn_lowbit_workspace_bytes(const qattn_problem_t* p) {
   Shape s;
   if (check_problem(p, &s) != QATTN_OK) return 0;

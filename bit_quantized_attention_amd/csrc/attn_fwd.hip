@@ -57,6 +57,7 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kKT = 64;             // keys per tile
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
@@ -114,6 +115,12 @@ struct FwdArgs {
   const uint16_t* k16;
   const float* k_mean;
   const int32_t* head_hi;
+  // promoted path with an MX FP4 low path: E2M1 codes (two per byte) and E8M0
+  // exponents (one per 32 channels) of the raw Q and the smoothed K
+  const uint8_t* q4;
+  const uint8_t* qe;
+  const uint8_t* k4;
+  const uint8_t* ke;
   // kv_idx / kv_cnt / max_keep hold key lists (gathered keys) instead of
   // block lists
   bool gather;
@@ -146,6 +153,16 @@ struct Geo {
   static constexpr int K16SLOTS = K16ROW / 16;
   static constexpr int KS16 = D / 16;
   static __device__ __forceinline__ int k16swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+  // MX FP4 low tiles: a K row is D/2 bytes of E2M1 codes (D/32 16-byte slots),
+  // the 4-bit product takes 64-channel k-steps, and the row's D/32 exponent
+  // bytes follow the tile in the tail. Swizzle: the 16 rows of a 16-lane read
+  // phase (same slot) cover all 64 banks.
+  static constexpr int K4ROW = D / 2;
+  static constexpr int K4SLOTS = D / 32;
+  static constexpr int K4BUF = kKT * K4ROW;
+  static constexpr int KS4 = D / 64;
+  static constexpr int K4EXP = D / 32;  // exponent bytes per key
+  static __device__ __forceinline__ int k4swz(int r) { return D == 128 ? ((r >> 2) & 3) : ((r >> 3) & 1); }
 };
 
 // 16 bytes per lane from global memory straight into LDS at
@@ -171,7 +188,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int D, bool BF16, bool CAUSAL, bool SPARSE, int QB, int NW, int WPE, int NBUF, bool PROMOTE,
-          bool GATHER>
+          bool GATHER, bool LOW4 = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_kernel(FwdArgs a) {
   using MM = Mma16<BF16>;
@@ -187,6 +204,9 @@ void attn_fwd_kernel(FwdArgs a) {
   // gathered keys: sparse layout; kv_idx holds key lists (max_keep entries per
   // query block) and a tile is 64 consecutive list entries
   static_assert(!GATHER || (SPARSE && QB == 1 && !PROMOTE), "gathered keys: sparse layout, QB = 1");
+  // MX FP4 low tiles: only on the promoted path
+  static_assert(!LOW4 || PROMOTE, "4-bit low tiles: promoted path");
+  static_assert(!LOW4 || (G::K4BUF + kKT * G::K4EXP <= G::KBUF + 256), "4-bit K tile fits the K slot");
   constexpr int KPIECES = G::KBUF / 1024;  // 1 KB direct loads per K tile
   constexpr int VPIECES = G::VBUF / 1024;
   // Staging buffer j (K tile, the tail carrying its scale, V tile) is one
@@ -411,7 +431,7 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // ---- Q fragments (B operand of S^T = K Q^T) -----------------------------------
   v4i qf[QB][G::KS];
-  if (wave_live) {
+  if (wave_live && !LOW4) {
     const int8_t* qg = a.q_i8 + (bhq * a.N + row0) * D;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -419,8 +439,23 @@ void attn_fwd_kernel(FwdArgs a) {
       for (int ks = 0; ks < G::KS; ++ks)
         qf[qb][ks] = *reinterpret_cast<const v4i*>(qg + (size_t)(32 * qb + l32) * D + 32 * ks + 16 * h);
   }
-  const float alpha_q = wave_live ? a.q_scale[bhq * a.nqb + qblk] * a.c : 0.0f;
-  const float* kscale = a.k_scale + (size_t)kvu * a.nkb;
+  const float alpha_q = (wave_live && !LOW4) ? a.q_scale[bhq * a.nqb + qblk] * a.c : 0.0f;
+  const float* kscale = LOW4 ? nullptr : a.k_scale + (size_t)kvu * a.nkb;
+  // 4-bit low tiles: the wave's query rows as MX FP4 B-operand fragments
+  // (lane (l32, h): row row0 + l32, channels 64 ks + 32 h + [0, 32)) and
+  // their exponents
+  v4i q4f[LOW4 ? G::KS4 : 1];
+  int q4e[LOW4 ? G::KS4 : 1];
+  if constexpr (LOW4) {
+    if (wave_live) {
+      const size_t qr = bhq * a.N + row0 + l32;
+#pragma unroll
+      for (int ks = 0; ks < G::KS4; ++ks) {
+        q4f[ks] = *reinterpret_cast<const v4i*>(a.q4 + qr * G::K4ROW + 32 * ks + 16 * h);
+        q4e[ks] = a.qe[qr * G::K4EXP + 2 * ks + h];
+      }
+    }
+  }
 
   v16f acc[G::DB][QB];
 #pragma unroll
@@ -463,6 +498,29 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int j = 0; j < KPW; ++j) {
       const int piece = (wave + NW * j) % KPIECES;
       lds_dma16(src + k_src_off(piece), buf + piece * 1024);
+    }
+  };
+  // 4-bit K tile t: KPW loads per wave like an INT8 tile (pieces repeat when
+  // the tile has fewer 1 KB pieces than the waves' loads; identical bytes)
+  auto load_k4 = [&](int t, int8_t* buf) {
+    constexpr int K4P = G::K4BUF / 1024;
+    const int8_t* src = reinterpret_cast<const int8_t*>(a.k4) + (kv_row0 + (size_t)t * kKT) * G::K4ROW;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int piece = (wave + NW * j) % K4P;
+      const int r = piece * (1024 / G::K4ROW) + lane / G::K4SLOTS;
+      lds_dma16(src + r * G::K4ROW + (((lane % G::K4SLOTS) ^ G::k4swz(r)) * 16), buf + piece * 1024);
+    }
+  };
+  // the tail word of a tile's stage: its K scale (INT8 tiles; all lanes the
+  // same word), or (4-bit low path) its 64 keys' exponent bytes, lane l
+  // bringing 4 of them (d = 64: 2 keys per word, lanes 32-63 repeat 0-31)
+  auto tail_dma = [&](int t, int8_t* kb) {
+    if constexpr (LOW4) {
+      const int w = D == 128 ? lane : (lane & 31);
+      lds_dma4(a.ke + (kv_row0 + (size_t)t * kKT) * G::K4EXP + 4 * w, kb + G::KBUF);
+    } else {
+      lds_dma4(kscale + t, kb + G::KBUF);
     }
   };
   auto tile_kscale = [&](const int8_t* buf) {
@@ -554,11 +612,12 @@ void attn_fwd_kernel(FwdArgs a) {
     }
     if constexpr (PROMOTE) {
       if (hs >= 0) load_k16(t, hs, kb);
+      else if constexpr (LOW4) load_k4(t, kb);
       else load_k(t, kb);
     } else {
       load_k(t, kb);
     }
-    lds_dma4(kscale + t, kb + G::KBUF);
+    tail_dma(t, kb);
     load_v(t, vb);
   };
   // Waits go through the s_waitcnt builtin (not inline asm) so that the
@@ -869,6 +928,93 @@ void attn_fwd_kernel(FwdArgs a) {
     });
   };
 
+  // ---- 4-bit low tiles (MX FP4 Q K^T, the promoted path's low path) -----------
+  // S^T = K4 . Q4^T on v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands and
+  // E8M0 scales per 32 channels (lane (l32, h): key row 32 kb + l32 and query
+  // row l32, channels 64 ks + 32 h + [0, 32)); the fp32 result has the S^T
+  // layout of the INT8 product. The products of E2M1 values are exact, and so
+  // is their fp32 sum unless the summed groups' exponents span more than about
+  // ten binades.
+  auto qk4 = [&](const int8_t* kbp, v16f (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = 32 * kb + l32;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < G::KS4; ++ks) {
+        const v4i kf = *reinterpret_cast<const v4i*>(kbp + r * G::K4ROW + (((2 * ks + h) ^ G::k4swz(r)) * 16));
+        const int ke = (int)*reinterpret_cast<const uint8_t*>(kbp + G::KBUF + r * G::K4EXP + 2 * ks + h);
+        const v8i ka = {kf[0], kf[1], kf[2], kf[3], 0, 0, 0, 0};
+        const v8i qa = {q4f[ks][0], q4f[ks][1], q4f[ks][2], q4f[ks][3], 0, 0, 0, 0};
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qa, s[kb], 4, 4, 0, ke, 0, q4e[ks]);
+      }
+    }
+  };
+  // Online softmax of a 4-bit tile: the logit of element (kb, r) is
+  // c * S (the smoothed keys put it in the INT8 path's frame), so the
+  // exponent is one fma, fma(c, S, -m). Element (kb, r) holds key
+  // t*64 + 32 kb + 8 (r/4) + 4 h + r%4. Reference rule, filter and rescale as
+  // in softmax.
+  auto softmax_f = [&](auto masked_c, const v16f (&s)[2], int t, op_t (&pf)[2][QB][2]) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int lim = (row0 + l32) - (t * kKT + 4 * h);
+    auto exps = [&](float m) -> float {
+      float lsum[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          op_t pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * hf + e;
+            const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(a.c, s[kb][r], -m));
+            if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
+            lsum[e & 3] += pe;
+            pk[e] = (el_t)pe;
+          }
+          pf[kb][0][hf] = pk;
+        }
+      return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    };
+    float psum = exps(m_ref[0]);
+    if (__ballot(psum > kSumFilter) != 0) {
+      float mxs = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          mxs = __builtin_fmaxf(mxs, (MASKED && off > lim) ? -__builtin_inff() : s[kb][r]);
+        }
+      {
+        const int mi = __builtin_bit_cast(int, mxs);
+        const auto sw = __builtin_amdgcn_permlane32_swap(mi, mi, false, false);
+        mxs = __builtin_fmaxf(__builtin_bit_cast(float, (int)sw[0]), __builtin_bit_cast(float, (int)sw[1]));
+      }
+      // c > 0: the max logit is the logit of the max product (-inf when the
+      // row sees no key of this tile)
+      const float mx = a.c * mxs;
+      const float m_old = m_ref[0];
+      const float mc = __builtin_fmaxf(m_old, mx);
+      const bool move = mc > m_old + kTau;
+      if (__ballot(move) != 0) {
+        const float corr =
+            move ? (m_old == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_old - mc)) : 1.0f;
+        m_ref[0] = move ? mc : m_old;
+        psum = exps(m_ref[0]);
+        l_run[0] *= corr;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][0][r] *= corr;
+      }
+    }
+    l_run[0] += psum;
+  };
+
   // ---- gathered tiles: a scale per key ----------------------------------------
   // Element (kb, r) of the lane's 32 keys is row kb*32 + 8*(r/4) + 4*h + r%4
   // of the tile, i.e. list entry 64*it + that row. Its logit is
@@ -1077,6 +1223,15 @@ void attn_fwd_kernel(FwdArgs a) {
         };
         softmax(masked_c, s, alpha, t, p_out, lagged_pv);
       }
+    } else if constexpr (LOW4) {
+      v16f s4[2];
+      if (wave_live) qk4(kbuf(cur), s4);
+      issue(tl, tl_hs, kbuf(nxt), vbuf(nxt));
+      if (wave_live) {
+        op_t p[2][QB][2];
+        softmax_f(masked_c, s4, t, p);
+        pv(vbuf(cur), p);
+      }
     } else {
       if (wave_live) {
         if constexpr (!GATHER) alpha = alpha_q * tile_kscale(kbuf(cur));
@@ -1143,7 +1298,7 @@ void attn_fwd_kernel(FwdArgs a) {
         v16f s;
         qk16(kbuf(cur), qf16, s);
         load_k16(tl, ul & 1, kbuf(nxt));
-        lds_dma4(kscale + tl, kbuf(nxt) + G::KBUF);
+        tail_dma(tl, kbuf(nxt));
         load_v(tl, vbuf(nxt));
         op_t p[2];
         softmax_hi(s, t * kKT + 32 * hs, cq, p);
@@ -1242,6 +1397,9 @@ hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
     if (a.gather) {
       hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, false, true>), grid,
                          dim3(4 * 64), 0, stream, a);
+    } else if (a.q16 != nullptr && a.k4 != nullptr) {
+      hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, true, false, true>), grid,
+                         dim3(4 * 64), 0, stream, a);
     } else if (a.q16 != nullptr) {
       hipLaunchKernelGGL((attn_fwd_kernel<D, BF16, CAUSAL, true, 1, 4, 2, 3, true, false>), grid,
                          dim3(4 * 64), 0, stream, a);
@@ -1277,8 +1435,12 @@ hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_sc
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
                            const void* q16, const void* k16, const float* k_mean,
                            const int32_t* head_hi, bool gather, void* o, float* lse,
-                           hipStream_t stream) {
+                           hipStream_t stream, const Fp4Codes* low4) {
   FwdArgs a;
+  a.q4 = low4 ? low4->q4 : nullptr;
+  a.qe = low4 ? low4->qe : nullptr;
+  a.k4 = low4 ? low4->k4 : nullptr;
+  a.ke = low4 ? low4->ke : nullptr;
   a.q_i8 = q_i8;
   a.q_scale = q_scale;
   a.k_i8 = k_i8;

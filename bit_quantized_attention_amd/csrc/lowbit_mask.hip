@@ -267,11 +267,10 @@ size_t lowbit_workspace_bytes(const Shape& s, bool with_scores) {
   return n;
 }
 
-hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, const float* k_mean,
-                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
-                              int32_t* kv_cnt, float* scores, void* workspace,
-                              hipStream_t stream) {
-  const LowbitLayout L = lowbit_layout(workspace, s, scores);
+namespace {
+
+void launch_quant(const Shape& s, const void* q, const void* k, const float* k_mean,
+                  const LowbitLayout& L, hipStream_t stream) {
   const long long nq_rows = (long long)s.B * s.Hq * s.N;
   const long long nk_rows = (long long)s.B * s.Hkv * s.N;
   const int rows_per_block = 256 / (s.d / 8);
@@ -293,6 +292,27 @@ hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, cons
       hipLaunchKernelGGL((mxfp4_quant_kernel<64, false>), dim3((unsigned)qgrid), dim3(256), 0,
                          stream, q16, k16, k_mean, L, nq_rows, nk_rows, s.N);
   }
+}
+
+}  // namespace
+
+Fp4Codes fp4_codes(void* workspace, const Shape& s) {
+  const LowbitLayout L = lowbit_layout(workspace, s, nullptr);
+  return Fp4Codes{L.q4, L.qe, L.k4, L.ke};
+}
+
+hipError_t launch_mxfp4_quant(const Shape& s, const void* q, const void* k, const float* k_mean,
+                              void* workspace, hipStream_t stream) {
+  launch_quant(s, q, k, k_mean, lowbit_layout(workspace, s, nullptr), stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, const float* k_mean,
+                              int keep_num, int keep_den, int max_keep, int32_t* kv_idx,
+                              int32_t* kv_cnt, float* scores, void* workspace,
+                              hipStream_t stream) {
+  const LowbitLayout L = lowbit_layout(workspace, s, scores);
+  launch_quant(s, q, k, k_mean, L, stream);
   ScoreArgs sa;
   sa.L = L;
   sa.B = s.B;

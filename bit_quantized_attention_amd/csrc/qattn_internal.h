@@ -71,16 +71,32 @@ hipError_t launch_lowbit_mask(const Shape& s, const void* q, const void* k, cons
 // most 64-key blocks (N / 64) the promoted path supports.
 int fwd_max_sparse_tiles();
 
+// MX FP4 codes and exponents of Q and the smoothed K (the low-bit workspace
+// layout): q4 [B*Hq*N][d/2], qe [B*Hq*N][d/32], k4 [B*Hkv*N][d/2],
+// ke [B*Hkv*N][d/32].
+struct Fp4Codes {
+  const uint8_t* q4;
+  const uint8_t* qe;
+  const uint8_t* k4;
+  const uint8_t* ke;
+};
+
 // Dense (kv_idx NULL), sparse (kv_idx set, q16 NULL), promoted (kv_idx, q16,
-// k16 and k_mean set), adaptive (head_hi, q16, k16 and k_mean set, kv_idx
-// NULL) or gathered-key (gather, kv_idx / kv_cnt / max_keep the key lists)
-// attention forward.
+// k16 and k_mean set; low4 set: the low tiles at MX FP4 instead of INT8),
+// adaptive (head_hi, q16, k16 and k_mean set, kv_idx NULL) or gathered-key
+// (gather, kv_idx / kv_cnt / max_keep the key lists) attention forward.
 hipError_t launch_attn_fwd(const Shape& s, const int8_t* q_i8, const float* q_scale,
                            const int8_t* k_i8, const float* k_scale, const void* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, int max_keep,
                            const void* q16, const void* k16, const float* k_mean,
                            const int32_t* head_hi, bool gather, void* o, float* lse,
-                           hipStream_t stream);
+                           hipStream_t stream, const Fp4Codes* low4 = nullptr);
+
+// MX FP4 quantization of the raw Q and the smoothed K into the low-bit
+// workspace, and the codes' addresses there.
+hipError_t launch_mxfp4_quant(const Shape& s, const void* q, const void* k, const float* k_mean,
+                              void* workspace, hipStream_t stream);
+Fp4Codes fp4_codes(void* workspace, const Shape& s);
 
 // Longest key list the gathered-key forward accepts (entries per query block).
 int fwd_max_gather_keys();

@@ -261,6 +261,40 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
                                   int32_t max_keep, void* o, float* lse, void* stream);
 
 /*
+ * qattn_fwd_promoted_fp4 -- promote instead of skip with an MX FP4 low path:
+ * the kept blocks at 16-bit Q K^T, every other visible block at 4-bit Q K^T.
+ *
+ * The ThriftAttention summary (gist.science/ja/paper/2605.23081), technical
+ * summary, method: the top-k block pairs at 16-bit precision, the remaining
+ * pairs in a 4-bit format (NVFP4 on the page's hardware), one online-softmax
+ * merge, the low blocks first. Here the 4-bit format is OCP MX FP4 (the
+ * format of qattn_block_mask_lowbit: E2M1 codes, one E8M0 exponent per 32
+ * channels) of the raw Q and the smoothed K, on CDNA4's FP4 matrix cores.
+ * Per (b, hq) and query block of 128 rows, the plan and order are those of
+ * qattn_fwd_promoted; a low 64-key tile's logit is
+ *   s = fl32(log2(e)/sqrt(d)) * S4, S4 the dot product of the dequantized
+ *   4-bit query and key vectors (exact in fp32 while the exponents of the
+ *   summed 32-channel groups span less than about ten binades),
+ * formed with one fma into the exponent; P is rounded to V's dtype and P V
+ * runs at 16 bits as on the INT8 path. The call first writes the MX FP4 codes
+ * of q and of k - k_mean into the workspace, then runs the forward.
+ * In:  q [B,Hq,N,d], k [B,Hkv,N,d], v [B,Hkv,N,d] in p->dtype; k_mean
+ *      [B,Hkv,d] f32 from qattn_smooth_quant; kv_idx [B,Hq,N/128,max_keep],
+ *      kv_cnt [B,Hq,N/128] int32 as for qattn_fwd_promoted.
+ * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
+ * workspace: device scratch of at least qattn_lowbit_workspace_bytes(p)
+ *      bytes, overwritten (its start holds the codes: the same layout as the
+ *      low-bit mask's); not to be shared with a concurrent call.
+ * Errors: NULL for any missing pointer but lse; SHAPE/UNSUPPORTED, also
+ *      UNSUPPORTED when N > 131072; ALIGN; ARG when max_keep < 1,
+ *      max_keep > 2048 or the workspace is too small; DEVICE.
+ */
+qattn_status_t qattn_fwd_promoted_fp4(const qattn_problem_t* p, const void* q, const void* k,
+                                      const float* k_mean, const void* v, const int32_t* kv_idx,
+                                      const int32_t* kv_cnt, int32_t max_keep, void* o, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * qattn_block_mask_lowbit -- per query block, the key blocks to keep, scored
  * from element-level 4-bit estimates.
  *

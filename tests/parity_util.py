@@ -108,12 +108,12 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def run_gpu(qa, p, t, sparse=None, pools=None, with_lse=True, promote=False):
+def run_gpu(qa, p, t, sparse=None, pools=None, with_lse=True, promote=False, low4=False):
     """The whole path on cuda:0 through the C ABI; returns (plan, o) on device."""
     dev = torch.device("cuda:0")
     q, k, v = (t[x].to(dev) for x in "qkv")
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
-                   sparse=sparse, with_lse=with_lse, pools=pools, promote=promote)
+                   sparse=sparse, with_lse=with_lse, pools=pools, promote=promote, low4=low4)
     o = torch.empty_like(q)
     plan.run(q, k, v, o)
     torch.cuda.synchronize()

@@ -92,6 +92,14 @@ def _fp(p, **over):
                                  args["mk"], args["o"], args["lse"], stream=0, check=False)
 
 
+def _f4(p, **over):
+    args = dict(q=A, k=A, km=A, v=A, idx=A, cnt=A, mk=8, o=A, lse=None, ws=A, wsb=1 << 40)
+    args.update(over)
+    return qa.qattn_fwd_promoted_fp4(p, args["q"], args["k"], args["km"], args["v"], args["idx"],
+                                     args["cnt"], args["mk"], args["o"], args["lse"], args["ws"],
+                                     args["wsb"], stream=0, check=False)
+
+
 def _he(p, **over):
     args = dict(qi=A, qs=A, ki=A, kscl=A, q=A, k=A, km=A, thr=0.02, err=A, hi=None)
     args.update(over)
@@ -228,6 +236,19 @@ def test_fwd_promoted_arguments(lib):
     assert _fp(_p(N=131072 + 128)) == UNSUP
 
 
+def test_fwd_promoted_fp4_arguments(lib):
+    p = _p(N=1024)
+    for name in ["q", "k", "km", "v", "idx", "cnt", "o", "ws"]:
+        assert _f4(p, **{name: None}) == NULL, name
+        assert _f4(p, **{name: A + 8}) == ALIGN, name
+    assert _f4(p, lse=A + 4) == ALIGN
+    assert _f4(p, mk=0) == ARG
+    assert _f4(p, mk=2049) == ARG
+    # the workspace holds the MX FP4 codes (the low-bit mask's layout)
+    assert _f4(p, wsb=qa.qattn_lowbit_workspace_bytes(p) - 4 * 8 * 16 * 4 - 1) == ARG
+    assert _f4(_p(N=131072 + 128)) == UNSUP
+
+
 def test_head_error_arguments(lib):
     p = _p()
     for name in ["qi", "qs", "ki", "kscl", "q", "k", "km", "err"]:
@@ -298,6 +319,7 @@ def test_max_keep_and_workspace_sizes(lib):
 
 def test_binding_has_the_c_names():
     for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
+              "qattn_fwd_promoted_fp4", "qattn_smooth_quant_noalloc",
               "qattn_head_error", "qattn_fwd_adaptive", "qattn_block_mask_lowbit",
               "qattn_lowbit_workspace_bytes", "qattn_stripe_select", "qattn_fwd_stripes",
               "qattn_workspace_bytes", "qattn_max_keep",

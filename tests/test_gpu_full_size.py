@@ -1,8 +1,10 @@
 """GPU parity at the full sizes of the workloads for the paths the benchmark
-times besides the dense and block-sparse forwards: the promoted forward
-(c2 and c5), the per-head error proxy and the adaptive forward (c2), and the
-element-level 4-bit block mask (c5). Same bars as the small cases; each side
-computes its own smoothing, quantization and lists, which are compared first.
+times besides the dense and block-sparse forwards: the promoted forward with
+its INT8 and its MX FP4 low path (the Llama-shaped causal N = 8192 workload and
+the block-sparse N = 32768 one), the per-head error proxy and the adaptive
+forward (N = 8192), and the element-level 4-bit block mask (N = 32768). Same
+bars as the small cases; each side computes its own smoothing, quantization
+and lists, which are compared first.
 """
 
 import numpy as np
@@ -17,7 +19,8 @@ from parity_util import (COS_MIN, log, cos, to_np, run_gpu, head_slice, same_lis
 
 pytestmark = pytest.mark.gpu
 
-ADAPTIVE_THRESHOLD = 0.019  # the c2 benchmark's setting: splits the heads of that law
+COS_MIN_FP4 = 0.98
+ADAPTIVE_THRESHOLD = 0.019  # the benchmark's setting at N = 8192: splits the heads of that law
 
 def _slices(p):
     """(b, kv head, query heads) of the first kv head of the first batch entry
@@ -28,12 +31,13 @@ def _slices(p):
         out.append((b, hk, hqs))
     return out
 
+@pytest.mark.parametrize("low4", [False, True], ids=["int8-low", "fp4-low"])
 @pytest.mark.parametrize("c", [2, 5])
-def test_promoted_full_size_sampled(gpu_lib, c):
+def test_promoted_full_size_sampled(gpu_lib, c, low4):
     p, t = make_config(c)
     keep = p.sparse if p.sparse is not None else (1, 10)
-    log(f"promoted full size: {p.name}, keep {keep}")
-    plan, o = run_gpu(gpu_lib, p, t, sparse=keep, pools=True, promote=True)
+    log(f"promoted full size ({'MX FP4' if low4 else 'INT8'} low path): {p.name}, keep {keep}")
+    plan, o = run_gpu(gpu_lib, p, t, sparse=keep, pools=True, promote=True, low4=low4)
     nqb = p.N // 128
     for b, hk, hqs in _slices(p):
         sub, _ = head_slice(t, p, b, hqs)
@@ -45,10 +49,15 @@ def test_promoted_full_size_sampled(gpu_lib, c):
         sel = [(0, n, i) for n in range(len(hqs)) for i in (0, nqb // 2, nqb - 1)
                if agree[0, n, i]]
         blocks = sorted({i for (_, _, i) in sel})
-        (_, pre, _), (_, pre0, _) = emulate_both(
-            oracle.emulate_promoted_attention, ref["q_i8"], ref["q_scale"], ref["k_i8"],
-            ref["k_scale"], sub["q"], sub["k"], ref["k_mean"], sub["v"], p.causal, len(hqs), 1,
-            idx, cnt, blocks=sel)
+        if low4:
+            (_, pre, _), (_, pre0, _) = emulate_both(
+                oracle.emulate_promoted_fp4_attention, sub["q"], sub["k"], ref["k_mean"],
+                sub["v"], p.causal, len(hqs), 1, idx, cnt, blocks=sel)
+        else:
+            (_, pre, _), (_, pre0, _) = emulate_both(
+                oracle.emulate_promoted_attention, ref["q_i8"], ref["q_scale"], ref["k_i8"],
+                ref["k_scale"], sub["q"], sub["k"], ref["k_mean"], sub["v"], p.causal, len(hqs),
+                1, idx, cnt, blocks=sel)
         ex, _ = oracle.exact_attention(sub["q"], sub["k"], sub["v"], p.causal, blocks=sel)
         rows = np.concatenate([np.arange(i * 128, i * 128 + 128) for i in blocks])
         g = to_np(o[b, hqs])[None][:, :, rows]
@@ -56,7 +65,8 @@ def test_promoted_full_size_sampled(gpu_lib, c):
                   f"b{b} kv head {hk}, {len(sel)} blocks: ", v=sub["v"])
         cc = cos(g, ex[:, :, rows])
         log(f"  cos_exact={cc:.6f}")
-        assert cc >= COS_MIN
+        # the 4-bit low path's Q K^T error is that of 4-bit codes
+        assert cc >= (COS_MIN_FP4 if low4 else COS_MIN)
 
 def _adaptive_gpu(qa, p, t):
     dev = torch.device("cuda:0")
@@ -73,7 +83,7 @@ def _adaptive_gpu(qa, p, t):
     torch.cuda.synchronize()
     return plan, err, hi, o
 
-def test_head_error_and_adaptive_full_size_c2(gpu_lib):
+def test_head_error_and_adaptive_full_size_n8192(gpu_lib):
     p, t = make_config(2)
     log(f"head error + adaptive full size: {p.name}, threshold {ADAPTIVE_THRESHOLD}")
     plan, err, hi, o = _adaptive_gpu(gpu_lib, p, t)
@@ -116,7 +126,7 @@ def test_head_error_and_adaptive_full_size_c2(gpu_lib):
         log(f"  cos_exact={cc:.6f}")
         assert cc >= COS_MIN
 
-def test_lowbit_mask_full_size_c5(gpu_lib):
+def test_lowbit_mask_full_size_n32768(gpu_lib):
     # the block-sparse workload (N = 32768): scores and kept lists of two query
     # heads, every query block, bit for bit
     qa = gpu_lib
