@@ -25,6 +25,9 @@ written for reading, not for speed:
 * ``lowbit_block_mask`` (module ``lowbit``) -- the element-level 4-bit
   block estimator: MX FP4 Q and smoothed K, the block score as the largest
   estimated product over the block's visible pairs, the same selection rule.
+* ``predict_patterns`` (module ``patterns``) -- vertical and slash lines
+  predicted from the votes of the per-query-block selections, added to every
+  query block's plan.
 * ``stripe_select`` / ``emulate_stripe_attention`` (module ``stripes``) --
   anchor-based stripe selection (keys within a threshold of the anchor taken
   over the initial tokens and the local window) and the quantized path over
@@ -47,7 +50,8 @@ Sources (the explainer pages these follow):
 * SALE explainer, aibr.jp/archives/118208, sections 1-3: a cheap low-bit
   estimate turned into a block-sparse plan that skips the rest, with the sink
   (first) and local (diagonal) stripes kept; element-level 4-bit estimates of
-  the query-key products.
+  the query-key products; vertical and slash lines predicted from the
+  attention map's tendencies.
 
 Parity pins: every function here is pinned by CPU tests against closed forms,
 invariants, a library routine that computes the same definition, or brute force
@@ -66,3 +70,4 @@ from .attention import (exact_attention, emulate_attention, emulate_promoted_att
 from .lowbit import lowbit_block_mask, lowbit_scores, mxfp4_quantize  # noqa: F401,E402
 from .stripes import stripe_select, emulate_stripe_attention  # noqa: F401,E402
 from .promote_fp4 import emulate_promoted_fp4_attention  # noqa: F401,E402
+from .patterns import predict_patterns, pattern_votes  # noqa: F401,E402
