@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
                     [--promote [--low4] | --adaptive TAU | --stripes THETA]
-                    [--mask pooled|lowbit]
+                    [--mask pooled|lowbit] [--patterns NV NS]
 
 A step is one pass of the whole path over one batch of the workload's seeded
 synthetic input (already resident in HBM): qattn_smooth_quant, then
@@ -30,7 +30,11 @@ attention launch time includes the call's MX FP4 quantization of Q and K.
 
 With ``--mask lowbit`` the kept lists come from qattn_block_mask_lowbit (the
 element-level 4-bit estimator) instead of qattn_block_mask (pooled block
-means); the mask launch is part of the step either way.
+means); the mask launch is part of the step either way. ``--patterns NV NS``
+adds qattn_block_mask_patterns to the step: each head's NV vertical and NS
+slash lines, predicted from the votes of the mask's selections, join every
+query block's kept list before the attention (its pairs are counted over the
+extended lists).
 
 With ``--adaptive TAU`` the step runs qattn_head_error after the smoothing
 (its per-head INT8 logit error on a fixed sample) and then qattn_fwd_adaptive:
@@ -192,6 +196,8 @@ def parse():
                     help="with --promote: the blocks not promoted at MX FP4 Q K^T instead of INT8")
     ap.add_argument("--mask", choices=["pooled", "lowbit"], default="pooled",
                     help="block scores from pooled block means or element-level 4-bit estimates")
+    ap.add_argument("--patterns", type=int, nargs=2, default=None, metavar=("NV", "NS"),
+                    help="extend the kept lists with NV vertical and NS slash lines per head")
     ap.add_argument("--adaptive", type=float, default=None, metavar="TAU",
                     help="per-head precision: heads whose sampled INT8 logit error exceeds TAU "
                          "(log2 units) run at 16-bit Q K^T")
@@ -303,7 +309,7 @@ def stripe_pairs(key_idx: np.ndarray, key_cnt: np.ndarray, causal: bool) -> floa
 
 
 def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, adaptive=None,
-                     mask: str = "pooled", stripes=None, low4: bool = False):
+                     mask: str = "pooled", stripes=None, low4: bool = False, patterns=None):
     """The oracle, as it stands, on a bounded sample: every query block of as many
     query heads as fit in about target_s seconds (after the head's group is
     smoothed and quantized, and masked when sparse)."""
@@ -331,6 +337,8 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
             num, den = keep
             idx, cnt, _ = oracle.block_mask(sq["q_pool"], sq["k_pool"], len(hqs), 1, p.causal,
                                             num, den)
+            if patterns is not None:
+                _, idx, cnt = oracle.predict_patterns(idx, cnt, p.N, p.causal, *patterns)
         if adaptive is not None:
             err = oracle.head_error(sq["q_i8"], sq["q_scale"], sq["k_i8"], sq["k_scale"], q, k,
                                     sq["k_mean"], len(hqs), 1)
@@ -341,6 +349,8 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
                 idx, cnt, _, _ = oracle.lowbit_block_mask(q, k, len(hqs), 1, p.causal, keep[0],
                                                           keep[1], k_mean=sq["k_mean"],
                                                           heads=[(0, n)])
+                if patterns is not None:
+                    _, idx, cnt = oracle.predict_patterns(idx, cnt, p.N, p.causal, *patterns)
             if stripes is not None:
                 theta, mk = stripes
                 sidx, scnt, _ = oracle.stripe_select(sq["q_pool"][:, n:n + 1], sq["k_i8"],
@@ -379,6 +389,7 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
         "kind": "oracle",
         "sample": f"oracle smooth_quant + "
                   f"{('lowbit_block_mask + ' if mask == 'lowbit' else 'block_mask + ') if sparse else ''}"
+                  f"{'predict_patterns + ' if patterns is not None else ''}"
                   f"{'head_error + ' if adaptive is not None else ''}"
                   f"{'stripe_select + emulate_stripe_attention' if stripes is not None else ('emulate_promoted_fp4_attention' if low4 else 'emulate_promoted_attention' if promote or adaptive is not None else 'emulate_attention')} "
                   f"over all {nqb} query blocks of {heads_done} query head(s) of batch 0 "
@@ -417,9 +428,12 @@ def main():
         keep = None
     else:
         keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
+    if args.patterns is not None and keep is None:
+        raise SystemExit("--patterns extends a block mask (a sparse workload or --promote)")
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
                    sparse=keep, promote=args.promote, low4=args.low4,
-                   pools=True if stripes else None)
+                   pools=True if stripes else None,
+                   patterns=tuple(args.patterns) if args.patterns is not None else None)
     o = torch.empty_like(q)
     head_err = torch.empty((p.B, p.Hq), dtype=torch.float32, device=dev)
     head_hi = torch.empty((p.B, p.Hq), dtype=torch.int32, device=dev)
@@ -433,8 +447,10 @@ def main():
 
     def block_mask():
         if lowbit_ws is not None:
-            qa.qattn_block_mask_lowbit(plan.p, q, k, plan.k_mean, keep[0], keep[1], plan.max_keep,
-                                       plan.kv_idx, plan.kv_cnt, None, lowbit_ws)
+            qa.qattn_block_mask_lowbit(plan.p, q, k, plan.k_mean, keep[0], keep[1], plan.mask_keep,
+                                       plan.mask_idx, plan.mask_cnt, None, lowbit_ws)
+            if args.patterns is not None:
+                plan.extend_patterns()
         else:
             plan.block_mask()
 
@@ -587,7 +603,9 @@ def main():
                    "low_path": ("mxfp4" if args.low4 else "int8") if args.promote else None,
                    "adaptive_threshold": args.adaptive,
                    "stripes": [args.stripes, args.stripe_keys] if stripes else None,
-                   "mask": args.mask if keep is not None else None, "input_dtype": p.dtype},
+                   "mask": args.mask if keep is not None else None,
+                   "patterns": list(args.patterns) if args.patterns is not None else None,
+                   "input_dtype": p.dtype},
         "roofline": {
             "bound": "mfma",
             "achieved": achieved,
@@ -623,7 +641,7 @@ def main():
         res["cpu_baseline"] = run_cpu_baseline(p, t, args.cpu_seconds, keep, args.promote,
                                                args.adaptive, args.mask,
                                                (args.stripes, args.stripe_keys) if stripes else None,
-                                               low4=args.low4)
+                                               low4=args.low4, patterns=args.patterns)
     print(json.dumps(res))
 
 

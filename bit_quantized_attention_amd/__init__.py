@@ -38,6 +38,8 @@ _STATUS = {0: "QATTN_OK", 1: "QATTN_ERR_NULL", 2: "QATTN_ERR_SHAPE", 3: "QATTN_E
 # size of the allocation-free smoothing entry point's static scratch
 # (QATTN_NOALLOC_SCRATCH_BYTES in include/qattn.h)
 NOALLOC_SCRATCH_BYTES = 16 << 20
+# Most vertical or slash lines per head (QATTN_MAX_PATTERN_LINES)
+MAX_PATTERN_LINES = 64
 
 _lib = None
 
@@ -89,6 +91,8 @@ def load(path: str = LIB_PATH):
     lib.qattn_lowbit_workspace_bytes.restype = sz
     lib.qattn_block_mask_lowbit.argtypes = [P, vp, vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.qattn_block_mask_lowbit.restype = ctypes.c_int
+    lib.qattn_block_mask_patterns.argtypes = [P, vp, vp, i32, i32, i32, vp, vp, i32, vp, vp]
+    lib.qattn_block_mask_patterns.restype = ctypes.c_int
     lib.qattn_stripe_select.argtypes = [P, vp, vp, vp, ctypes.c_float, i32, vp, vp, vp]
     lib.qattn_stripe_select.restype = ctypes.c_int
     lib.qattn_fwd_stripes.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -250,6 +254,16 @@ def qattn_block_mask_lowbit(p, q, k, k_mean, keep_num, keep_den, max_keep, kv_id
     return st
 
 
+def qattn_block_mask_patterns(p, kv_idx, kv_cnt, max_keep, n_vertical, n_slash, kv_idx_out,
+                              kv_cnt_out, max_keep_out, lines, stream=None, check=True) -> int:
+    st = load().qattn_block_mask_patterns(ctypes.byref(p), _ptr(kv_idx), _ptr(kv_cnt), max_keep,
+                                          n_vertical, n_slash, _ptr(kv_idx_out), _ptr(kv_cnt_out),
+                                          max_keep_out, _ptr(lines), _stream(stream))
+    if check:
+        _check(st, "qattn_block_mask_patterns")
+    return st
+
+
 def qattn_stripe_select(p, q_pool, k_i8, k_scale, theta, max_keys, key_idx, key_cnt,
                         stream=None, check=True) -> int:
     st = load().qattn_stripe_select(ctypes.byref(p), _ptr(q_pool), _ptr(k_i8), _ptr(k_scale),
@@ -300,6 +314,8 @@ class Plan:
     ``promote`` the kept blocks are computed at 16-bit Q K^T and every other
     block through the INT8 path, instead of being skipped; ``low4`` (with
     ``promote``) takes those other blocks at MX FP4 Q K^T instead of INT8.
+    ``patterns`` = (n_vertical, n_slash) extends the mask's kept lists with
+    each head's predicted vertical and slash lines before the attention.
     """
 
     p: qattn_problem_t
@@ -309,6 +325,7 @@ class Plan:
     pools: Optional[bool] = None  # pooled block means; default: only when sparse
     promote: bool = False
     low4: bool = False
+    patterns: Optional[Tuple[int, int]] = None
 
     def __post_init__(self):
         import torch
@@ -340,6 +357,17 @@ class Plan:
                 raise ValueError(f"invalid keep ratio {self.sparse}")
             self.kv_idx = torch.empty((B, Hq, nqb, self.max_keep), dtype=torch.int32, **e)
             self.kv_cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, **e)
+        # the mask's own lists (the attention's lists unless patterns extend them)
+        self.mask_keep, self.mask_idx, self.mask_cnt = self.max_keep, self.kv_idx, self.kv_cnt
+        self.lines = None
+        if self.patterns is not None:
+            if self.sparse is None:
+                raise ValueError("patterns extend a block mask: a keep ratio is needed")
+            nv, ns = self.patterns
+            self.lines = torch.empty((B, Hq, max(1, nv + ns)), dtype=torch.int32, **e)
+            self.max_keep = min(nkb, self.mask_keep + nv + ns)
+            self.kv_idx = torch.empty((B, Hq, nqb, self.max_keep), dtype=torch.int32, **e)
+            self.kv_cnt = torch.empty((B, Hq, nqb), dtype=torch.int32, **e)
         self.lse = torch.empty((B, Hq, N), dtype=torch.float32, **e) if self.with_lse else None
         self.workspace4 = None
         if self.low4:
@@ -352,8 +380,17 @@ class Plan:
 
     def block_mask(self, stream=None):
         num, den = self.sparse
-        qattn_block_mask(self.p, self.q_pool, self.k_pool, num, den, self.max_keep, self.kv_idx,
-                         self.kv_cnt, self.workspace, stream=stream)
+        qattn_block_mask(self.p, self.q_pool, self.k_pool, num, den, self.mask_keep,
+                         self.mask_idx, self.mask_cnt, self.workspace, stream=stream)
+        if self.patterns is not None:
+            self.extend_patterns(stream)
+
+    def extend_patterns(self, stream=None):
+        """The mask's lists extended by each head's vertical and slash lines."""
+        nv, ns = self.patterns
+        qattn_block_mask_patterns(self.p, self.mask_idx, self.mask_cnt, self.mask_keep, nv, ns,
+                                  self.kv_idx, self.kv_cnt, self.max_keep, self.lines,
+                                  stream=stream)
 
     def fwd(self, v, o, stream=None):
         qattn_fwd(self.p, self.q_i8, self.q_scale, self.k_i8, self.k_scale, v, self.kv_idx,

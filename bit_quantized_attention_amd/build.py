@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqattn.so")
 PEAKS_LIB = os.path.join(PKG, "libqattn_peaks.so")
 SOURCES = ["smooth_quant.hip", "block_mask.hip", "attn_fwd.hip", "head_error.hip", "lowbit_mask.hip",
-           "stripes.hip",
+           "stripes.hip", "patterns.hip",
            "api.cpp"]
 ARCH = "gfx950"
 

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -233,6 +234,41 @@ qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, 
   return launched(qattn::launch_lowbit_mask(s, q, k, k_mean, keep_num, keep_den, max_keep, kv_idx,
                                             kv_cnt, scores, workspace,
                                             static_cast<hipStream_t>(stream)));
+}
+
+qattn_status_t qattn_block_mask_patterns(const qattn_problem_t* p, const int32_t* kv_idx,
+                                         const int32_t* kv_cnt, int32_t max_keep,
+                                         int32_t n_vertical, int32_t n_slash, int32_t* kv_idx_out,
+                                         int32_t* kv_cnt_out, int32_t max_keep_out,
+                                         int32_t* lines, void* stream) {
+  Shape s;
+  const qattn_status_t st = check_problem(p, &s);
+  if (st != QATTN_OK) return st;
+  if (s.nkb() > qattn::pattern_max_nkb()) return QATTN_ERR_UNSUPPORTED;
+  if (!kv_idx || !kv_cnt || !kv_idx_out || !kv_cnt_out) return QATTN_ERR_NULL;
+  if (n_vertical + n_slash > 0 && !lines) return QATTN_ERR_NULL;
+  const void* ptrs[] = {kv_idx, kv_cnt, kv_idx_out, kv_cnt_out, lines};
+  for (const void* x : ptrs)
+    if (x && misaligned(x)) return QATTN_ERR_ALIGN;
+  if (n_vertical < 0 || n_vertical > QATTN_MAX_PATTERN_LINES || n_slash < 0 ||
+      n_slash > QATTN_MAX_PATTERN_LINES)
+    return QATTN_ERR_ARG;
+  if (max_keep < 1) return QATTN_ERR_ARG;
+  const long long need = std::min<long long>(s.nkb(), (long long)max_keep + n_vertical + n_slash);
+  if (max_keep_out < need) return QATTN_ERR_ARG;
+  // the outputs are written while other rows' inputs are still read
+  const size_t rows = (size_t)s.B * s.Hq * s.nqb();
+  const auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+  };
+  const size_t in_b = rows * (size_t)max_keep * 4, out_b = rows * (size_t)max_keep_out * 4;
+  if (overlap(kv_idx, in_b, kv_idx_out, out_b) || overlap(kv_cnt, rows * 4, kv_cnt_out, rows * 4) ||
+      overlap(kv_idx, in_b, kv_cnt_out, rows * 4) || overlap(kv_cnt, rows * 4, kv_idx_out, out_b))
+    return QATTN_ERR_ARG;
+  return launched(qattn::launch_patterns(s, kv_idx, kv_cnt, max_keep, n_vertical, n_slash,
+                                         kv_idx_out, kv_cnt_out, max_keep_out, lines,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 qattn_status_t qattn_stripe_select(const qattn_problem_t* p, const float* q_pool,

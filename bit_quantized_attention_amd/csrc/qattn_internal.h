@@ -98,6 +98,16 @@ hipError_t launch_mxfp4_quant(const Shape& s, const void* q, const void* k, cons
                               void* workspace, hipStream_t stream);
 Fp4Codes fp4_codes(void* workspace, const Shape& s);
 
+// Most key blocks (N / 64) the pattern prediction supports.
+int pattern_max_nkb();
+
+// Vertical / slash lines of every (b, hq) from the votes of its kept lists
+// (lines [B*Hq][n_vertical + n_slash]) and the lists extended by them.
+hipError_t launch_patterns(const Shape& s, const int32_t* kv_idx, const int32_t* kv_cnt,
+                           int max_keep, int n_vertical, int n_slash, int32_t* kv_idx_out,
+                           int32_t* kv_cnt_out, int max_keep_out, int32_t* lines,
+                           hipStream_t stream);
+
 // Longest key list the gathered-key forward accepts (entries per query block).
 int fwd_max_gather_keys();
 

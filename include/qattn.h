@@ -300,8 +300,9 @@ qattn_status_t qattn_fwd_promoted_fp4(const qattn_problem_t* p, const void* q, c
  *
  * The SALE explainer (aibr.jp/archives/118208), sections 2 and 3: every
  * query-key product is estimated with 4-bit quantized Q and K, the estimates
- * are turned into a block-sparse plan, and the sink and local (vertical and
- * slash) patterns are kept. This library computes, per (b, hq):
+ * are turned into a block-sparse plan, and the sink and local patterns are
+ * kept (qattn_block_mask_patterns adds the predicted vertical and slash lines
+ * to such a plan). This library computes, per (b, hq):
  *   the raw Q and the smoothed K, Ks = fl32(K) - k_mean, in OCP MX FP4: per 32
  *   consecutive channels a shared exponent E = floor(log2 amax) - 2 (at least
  *   -127; -127 for an all-zero group) and E2M1 elements, x / 2^E rounded to
@@ -331,6 +332,46 @@ qattn_status_t qattn_block_mask_lowbit(const qattn_problem_t* p, const void* q, 
                                        int32_t max_keep, int32_t* kv_idx, int32_t* kv_cnt,
                                        float* scores, void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/*
+ * qattn_block_mask_patterns -- add the predicted vertical and slash lines of
+ * each head to every query block's kept list.
+ *
+ * The SALE explainer (aibr.jp/archives/118208), sections 1 and 3: the method
+ * also predicts vertical lines (key positions every query needs) and slash
+ * lines (a fixed query-key distance) from the attention map's tendencies.
+ * Here the tendencies are the votes of the per-query-block selections. Per
+ * (b, hq), with i a query block (128 rows) and j a key block (64 keys):
+ *   kept(i) = the entries among the first min(kv_cnt, max_keep) of list i
+ *     that are valid key blocks for i (0 <= j < N/64; j <= 2i + 1 when
+ *     causal), once each;
+ *   forced(i) = {0, 2i, 2i + 1} (the blocks every plan of qattn_block_mask
+ *     holds by rule, which carry no information);
+ *   each j in kept(i) \ forced(i) gives one vote to key block j (vertical)
+ *     and one to offset o = 2i - j (slash; negative past the diagonal);
+ *   the lines are the n_vertical key blocks and the n_slash offsets with the
+ *     most votes, at least two each, ties to the lower block or offset;
+ *   out(i) = kept(i), the valid vertical blocks and the valid blocks 2i - o
+ *     of the slash offsets, ascending.
+ * In:  kv_idx [B,Hq,N/128,max_keep], kv_cnt [B,Hq,N/128] int32 (e.g. from
+ *      qattn_block_mask or qattn_block_mask_lowbit).
+ * Out: kv_idx_out [B,Hq,N/128,max_keep_out] (ascending, then -1),
+ *      kv_cnt_out [B,Hq,N/128]; lines [B,Hq,n_vertical + n_slash] int32: the
+ *      vertical blocks in rank order (-1 where fewer qualify), then the slash
+ *      offsets in rank order (INT32_MIN where fewer qualify). The outputs must
+ *      not overlap the inputs. lines may be NULL when no line is asked for.
+ * Errors: NULL; SHAPE/UNSUPPORTED, also UNSUPPORTED when N > 131072; ALIGN;
+ *      ARG when n_vertical or n_slash is outside [0, QATTN_MAX_PATTERN_LINES],
+ *      max_keep < 1, max_keep_out < min(N/64, max_keep + n_vertical +
+ *      n_slash), or an output overlaps an input; DEVICE.
+ */
+#define QATTN_MAX_PATTERN_LINES 64
+
+qattn_status_t qattn_block_mask_patterns(const qattn_problem_t* p, const int32_t* kv_idx,
+                                         const int32_t* kv_cnt, int32_t max_keep,
+                                         int32_t n_vertical, int32_t n_slash, int32_t* kv_idx_out,
+                                         int32_t* kv_cnt_out, int32_t max_keep_out,
+                                         int32_t* lines, void* stream);
 
 /*
  * qattn_stripe_select -- per query block, the key positions within a

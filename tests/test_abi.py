@@ -100,6 +100,15 @@ def _f4(p, **over):
                                      args["wsb"], stream=0, check=False)
 
 
+def _pm(p, **over):
+    args = dict(idx=A, cnt=A, mk=8, nv=4, ns=4, oidx=A + (1 << 24), ocnt=A + (2 << 24), omk=16,
+                lines=A + (3 << 24))
+    args.update(over)
+    return qa.qattn_block_mask_patterns(p, args["idx"], args["cnt"], args["mk"], args["nv"],
+                                        args["ns"], args["oidx"], args["ocnt"], args["omk"],
+                                        args["lines"], stream=0, check=False)
+
+
 def _he(p, **over):
     args = dict(qi=A, qs=A, ki=A, kscl=A, q=A, k=A, km=A, thr=0.02, err=A, hi=None)
     args.update(over)
@@ -249,6 +258,29 @@ def test_fwd_promoted_fp4_arguments(lib):
     assert _f4(_p(N=131072 + 128)) == UNSUP
 
 
+def test_block_mask_patterns_arguments(lib):
+    p = _p(N=1024)   # 16 key blocks
+    for name in ["idx", "cnt", "oidx", "ocnt", "lines"]:
+        assert _pm(p, **{name: None}) == NULL, name
+        assert _pm(p, **{name: (A + 4) if name in ("idx", "cnt") else _pm_addr(name) + 4}) == ALIGN
+    # no line asked for: lines may be NULL (not called with valid arguments
+    # here: every other check must fail first)
+    assert _pm(p, nv=0, ns=0, lines=None, omk=7) == ARG
+    assert _pm(p, nv=-1) == ARG
+    assert _pm(p, ns=qa.MAX_PATTERN_LINES + 1) == ARG
+    assert _pm(p, mk=0) == ARG
+    assert _pm(p, omk=15) == ARG            # below max_keep + n_vertical + n_slash
+    assert _pm(_p(N=256), mk=3, omk=3) == ARG   # 4 key blocks: at least 4
+    # an output overlapping an input
+    assert _pm(p, oidx=A + 64) == ARG
+    assert _pm(p, ocnt=A) == ARG
+    assert _pm(_p(N=131072 + 128)) == UNSUP
+
+
+def _pm_addr(name):
+    return {"oidx": A + (1 << 24), "ocnt": A + (2 << 24), "lines": A + (3 << 24)}[name]
+
+
 def test_head_error_arguments(lib):
     p = _p()
     for name in ["qi", "qs", "ki", "kscl", "q", "k", "km", "err"]:
@@ -319,7 +351,7 @@ def test_max_keep_and_workspace_sizes(lib):
 
 def test_binding_has_the_c_names():
     for n in ["qattn_smooth_quant", "qattn_block_mask", "qattn_fwd", "qattn_fwd_promoted",
-              "qattn_fwd_promoted_fp4", "qattn_smooth_quant_noalloc",
+              "qattn_fwd_promoted_fp4", "qattn_smooth_quant_noalloc", "qattn_block_mask_patterns",
               "qattn_head_error", "qattn_fwd_adaptive", "qattn_block_mask_lowbit",
               "qattn_lowbit_workspace_bytes", "qattn_stripe_select", "qattn_fwd_stripes",
               "qattn_workspace_bytes", "qattn_max_keep",
@@ -346,3 +378,4 @@ def test_binding_constants_match_the_header():
     assert int(defs["QATTN_SOFTMAX_REF_THRESHOLD"]) == qa.SOFTMAX_REF_THRESHOLD
     assert "#define QATTN_NOALLOC_SCRATCH_BYTES (16u << 20)" in text
     assert qa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert int(defs["QATTN_MAX_PATTERN_LINES"]) == qa.MAX_PATTERN_LINES
