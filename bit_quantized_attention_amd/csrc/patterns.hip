@@ -12,11 +12,12 @@
 // set plus the valid blocks on those lines, in ascending order.
 //
 // Two launches:
-//  1. pattern_vote_kernel, one 256-thread workgroup per (b, hq): each wave
-//     takes every fourth query block, marks the block's valid entries in its
-//     own LDS bit set and adds one vote per marked, non-forced block to the
-//     head's counters in LDS; then the lines, one workgroup argmax per line
-//     over packed keys (votes << 16 | (65535 - index)), written to `lines`.
+//  1. pattern_vote_kernel, one 1024-thread workgroup per (b, hq): each of
+//     its 16 waves takes every sixteenth query block, marks the block's
+//     valid entries in its own LDS bit set and adds one vote per marked,
+//     non-forced block to the head's counters in LDS; then the lines, one
+//     workgroup argmax per line over packed keys (votes << 16 |
+//     (65535 - index)), written to `lines`.
 //  2. pattern_extend_kernel, one wave per (b, hq, query block): the bit set
 //     of the block's valid entries and the valid blocks on its head's lines,
 //     compacted in ascending order with popcounts and a wave prefix sum.
@@ -30,8 +31,10 @@ namespace {
 
 constexpr int kMaxNkb = 2048;           // key blocks (N <= 131072)
 constexpr int kWords = kMaxNkb / 32;    // bit-set dwords, one per lane
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;           // extend: one wave per query block
 constexpr int kWaves = kThreads / 64;
+constexpr int kVoteThreads = 1024;      // votes: 16 waves share a head's query blocks
+constexpr int kVoteWaves = kVoteThreads / 64;
 
 struct PatArgs {
   const int32_t* kv_idx;
@@ -86,18 +89,18 @@ __device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
   return v;
 }
 
-__global__ __launch_bounds__(kThreads) void pattern_vote_kernel(PatArgs a) {
+__global__ __launch_bounds__(kVoteThreads) void pattern_vote_kernel(PatArgs a) {
   __shared__ int vert[kMaxNkb];
   __shared__ int slash[2 * kMaxNkb];
-  __shared__ uint32_t bits[kWaves][kWords];
-  __shared__ unsigned red[kWaves];
+  __shared__ uint32_t bits[kVoteWaves][kWords];
+  __shared__ unsigned red[kVoteWaves];
   const int head = blockIdx.x;  // b * Hq + hq
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nslash = 2 * a.nkb - 1;
-  for (int x = tid; x < a.nkb; x += kThreads) vert[x] = 0;
-  for (int x = tid; x < nslash; x += kThreads) slash[x] = 0;
+  for (int x = tid; x < a.nkb; x += kVoteThreads) vert[x] = 0;
+  for (int x = tid; x < nslash; x += kVoteThreads) slash[x] = 0;
   __syncthreads();
-  for (int i = wave; i < a.nqb; i += kWaves) {
+  for (int i = wave; i < a.nqb; i += kVoteWaves) {
     const size_t r = (size_t)head * a.nqb + i;
     uint32_t w = mark_list(a, a.kv_idx + r * a.max_keep, a.kv_cnt[r], i, bits[wave], lane);
     w &= ~forced_word(i, lane, a.nkb, a.causal);
@@ -118,14 +121,16 @@ __global__ __launch_bounds__(kThreads) void pattern_vote_kernel(PatArgs a) {
     const int want = kind == 0 ? a.n_v : a.n_s;
     for (int r = 0; r < want; ++r) {
       unsigned best = 0u;
-      for (int x = tid; x < n; x += kThreads) {
+      for (int x = tid; x < n; x += kVoteThreads) {
         const int v = cnt[x];
         if (v >= 2) best = max(best, ((unsigned)v << 16) | (unsigned)(65535 - x));
       }
       best = wave_max_u32(best);
       if (lane == 0) red[wave] = best;
       __syncthreads();
-      best = max(max(red[0], red[1]), max(red[2], red[3]));
+      best = 0u;
+#pragma unroll
+      for (int w = 0; w < kVoteWaves; ++w) best = max(best, red[w]);
       const int x = 65535 - (int)(best & 0xffffu);
       if (tid == 0) {
         if (kind == 0) out[r] = best != 0u ? x : -1;
@@ -201,7 +206,7 @@ hipError_t launch_patterns(const Shape& s, const int32_t* kv_idx, const int32_t*
   a.n_s = n_slash;
   a.rows = s.B * s.Hq * a.nqb;
   a.causal = s.causal != 0;
-  hipLaunchKernelGGL(pattern_vote_kernel, dim3(s.B * s.Hq), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(pattern_vote_kernel, dim3(s.B * s.Hq), dim3(kVoteThreads), 0, stream, a);
   hipLaunchKernelGGL(pattern_extend_kernel, dim3((a.rows + kWaves - 1) / kWaves), dim3(kThreads),
                      0, stream, a);
   return hipGetLastError();
