@@ -464,15 +464,11 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.0f;
-  // l_run: this lane's half of the row sum; d_run: its sum of P times the
-  // rounding shift of the INT8 tiles' exponent constant (log2 units), which
-  // restores the exact lse to first order (see the INT8 softmax)
-  float m_ref[QB], l_run[QB], d_run[QB];
+  float m_ref[QB], l_run[QB];  // l_run: this lane's half of the row sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = -__builtin_inff();
     l_run[qb] = 0.0f;
-    d_run[qb] = 0.0f;
   }
 
   // ---- staging: direct global -> LDS, 1 KB per wave instruction -------------------
@@ -677,20 +673,12 @@ void attn_fwd_kernel(FwdArgs a) {
   // softmax of one tile, one 32-query block at a time: S (as 1.5*2^23 + S in
   // fp32) -> P packed in the B-operand layout of the P V product, the lane's
   // partial row sum (fp32, of P before its 16-bit rounding) added to l.
-  // The exponent alpha*S - m is one fma, fma(alpha, Sb, -C) with
-  // C = fl32(alpha * 1.5*2^23 + m) (formed from the exact split A_hi + A_lo
-  // of alpha * 1.5*2^23). Rounding C moves every exponent of the row in this
-  // tile by the same amount, at most half an ulp of C: at most alpha in log2
-  // units while m < alpha * 2^23 (|S| < 2^22 bounds every logit by that), so
-  // P and its share of l both change by a factor within 2^(+-alpha). alpha is
-  // the logit of one unit of S (about 1e-4 for logits of order ten), so the
-  // output moves by a reweighting of tiles far below the 16-bit rounding of
-  // P. The bias subtraction this saves was one of about five vector
-  // instructions per score. The shift itself, delta = C - (alpha*1.5*2^23 +
-  // m), is exact to first order ((C - A_hi) is exact, C being the rounded sum
-  // of A_hi and the smaller m + A_lo), and P's sum times delta goes to d_run:
-  // the exact row sum is sum_t 2^delta_t l_t = l + ln2 * d_run to first
-  // order, so lse takes d_run / l on top of m + log2(l).
+  // With A = alpha * 1.5*2^23 split into A_hi + A_lo (exact), the fma
+  // alpha*Sb - A_hi is alpha*S + A_lo, so the exponent alpha*S - m is
+  // fma(alpha, Sb, -A_hi) - (m + A_lo): two roundings of numbers of the size
+  // of the exponent itself. (One fma against a rounded A + m would shift a
+  // tile's exponents by up to alpha/2, enough to flip the 16-bit rounding of
+  // many P.)
   // The reference m follows the rule of the module comment, but the row max
   // is only formed when some lane's partial sum exceeds kSumFilter: a move
   // needs an element more than kTau above m, i.e. a P above 2^kTau. Then the
@@ -712,7 +700,7 @@ void attn_fwd_kernel(FwdArgs a) {
       // P against reference m (-inf: every visible P is +inf, which forces
       // the row max below), and its partial sum
       auto exps = [&](float m, float ahi, auto&& grp_hook) -> float {
-        const float nc = -(ahi + (m + a_lo));
+        const float cm = m + a_lo;
         // -0 is the additive identity, so the first additions fold away
         float lsum[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
         static_for<0, 4>([&](auto gc) {
@@ -726,7 +714,7 @@ void attn_fwd_kernel(FwdArgs a) {
               const int r = 8 * half + e;
               const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
               const float sb = __builtin_bit_cast(float, (int)s[kb][qb][r]);
-              const float x = __builtin_fmaf(alpha, sb, nc);
+              const float x = __builtin_fmaf(alpha, sb, -ahi) - cm;
               float pe = __builtin_amdgcn_exp2f(x);
               if constexpr (MASKED) pe = off > lim ? 0.0f : pe;
               lsum[e & 3] += pe;
@@ -777,7 +765,6 @@ void attn_fwd_kernel(FwdArgs a) {
           asm volatile("" : "+v"(ahi));
           psum = exps(m_ref[qb], ahi, [](auto, auto) {});
           l_run[qb] *= corr;
-          d_run[qb] *= corr;
 #pragma unroll
           for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -785,15 +772,6 @@ void attn_fwd_kernel(FwdArgs a) {
         }
       }
       l_run[qb] += psum;
-      {
-        // this tile's shift of the exponent constant for the final reference
-        // (none while the row has seen no key: then psum is 0)
-        const float m = m_ref[qb];
-        const float mal = m + a_lo;
-        const float c = a_hi + mal;
-        const float dlt = m == -__builtin_inff() ? 0.0f : (c - a_hi) - mal;
-        d_run[qb] = __builtin_fmaf(psum, dlt, d_run[qb]);
-      }
     });
   };
 
@@ -923,7 +901,6 @@ void attn_fwd_kernel(FwdArgs a) {
         m_ref[0] = move ? mc : m_old;
         psum = exps(m_ref[0]);
         l_run[0] *= corr;
-        d_run[0] *= corr;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -1029,7 +1006,6 @@ void attn_fwd_kernel(FwdArgs a) {
         m_ref[0] = move ? mc : m_old;
         psum = exps(m_ref[0]);
         l_run[0] *= corr;
-        d_run[0] *= corr;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -1123,7 +1099,6 @@ void attn_fwd_kernel(FwdArgs a) {
         m_ref[0] = move ? mc : m_old;
         psum = exps(m_ref[0]);
         l_run[0] *= corr;
-        d_run[0] *= corr;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -1368,7 +1343,6 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-    const float dt = d_run[qb] + __shfl_xor(d_run[qb], 32, 64);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int q = row0 + 32 * qb + l32;
     uint16_t* og = a.o + (bhq * a.N + q) * D;
@@ -1389,8 +1363,7 @@ void attn_fwd_kernel(FwdArgs a) {
       }
     if (a.lse != nullptr && h == 0) {
       a.lse[bhq * a.N + q] =
-          lt > 0.0f ? 0.69314718055994531f * (m_ref[qb] + __builtin_log2f(lt) + dt * inv)
-                    : -__builtin_inff();
+          lt > 0.0f ? 0.69314718055994531f * (m_ref[qb] + __builtin_log2f(lt)) : -__builtin_inff();
     }
   }
 }
