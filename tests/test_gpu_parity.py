@@ -89,6 +89,36 @@ def test_smooth_quant_exact_ties(gpu_lib, dtype, d):
         assert bad == 0, f"{key}: {bad} of {got.size} differ"
 
 
+def test_smooth_quant_wide_range_bf16(gpu_lib):
+    """bf16 K and Q whose magnitudes span 2^-61 .. 2^1 within every channel (a
+    ratio of 2^62, inside the 2^64 the header states for exact sums): the
+    channel means, pooled means, scales and codes are still bit-exact against
+    the oracle's math.fsum sums, which need the double-double's low word
+    (62 binades do not fit the 53 bits of one double)."""
+    p, t = make_case(B=1, Hq=2, Hkv=1, N=1024, d=64, dtype="bf16", causal=True, seed=33)
+    gen = torch.Generator().manual_seed(33)
+
+    def wide(shape):
+        e = torch.randint(-61, 1, shape, generator=gen).double()
+        m = 1.0 + torch.randint(0, 128, shape, generator=gen).double() / 128.0
+        sgn = torch.where(torch.rand(shape, generator=gen) < 0.5, -1.0, 1.0).double()
+        return (sgn * m * torch.exp2(e)).to(torch.bfloat16)
+
+    t["q"] = wide((1, p.Hq, p.N, p.d)).contiguous()
+    t["k"] = wide((1, p.Hkv, p.N, p.d)).contiguous()
+    a = t["k"][0, 0].double().abs()
+    for c in range(p.d):
+        nz = a[:, c][a[:, c] > 0]
+        assert float(nz.max() / nz.min()) < 2.0 ** 64
+    log("smooth_quant wide-range bf16")
+    plan, _ = run_gpu(gpu_lib, p, t, pools=True)
+    ref = oracle.smooth_quant(t["q"], t["k"], pools=True)
+    for key in ["k_mean", "q_scale", "k_scale", "q_pool", "k_pool", "q_i8", "k_i8"]:
+        got = to_np(getattr(plan, key))
+        bad = np.count_nonzero(got != ref[key])
+        assert bad == 0, f"{key}: {bad} of {got.size} differ"
+
+
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_fwd_matches_emulation_and_exact(gpu_lib, name, kw):
     p, t = _case(name, kw)
