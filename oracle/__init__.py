@@ -54,10 +54,11 @@ Sources (the explainer pages these follow):
   attention map's tendencies.
 
 Parity pins: every function here is pinned by CPU tests against closed forms,
-invariants, a library routine that computes the same definition, or brute force
-(tests/test_oracle_*.py). The floating-point tail of ``emulate_attention``
-beyond what those pins fix (the exact value of each exp2 rounding) is not
-pinned by any printed value: the pages print no worked example.
+invariants, a library routine that computes the same definition, brute force
+or hand-worked cases (tests/test_oracle_*.py, tests/golden/). The pages print
+no worked example, so no pin is a printed value; the exponentials are numpy's
+fp64 exp2 rounded once to fp32, checked by the closed forms up to that
+rounding.
 """
 
 from .rounding import bf16_rne, f16_rne, round_to_dtype  # noqa: F401
