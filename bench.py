@@ -10,6 +10,11 @@ qattn_block_mask for the block-sparse workload, then qattn_fwd. The default
 workload is the Llama-3.1-8B-shaped causal prefill (B=1, Hq=32, Hkv=8,
 N=8192, d=128, bf16).
 
+Before the W counted warmup steps, whole steps run untimed for at least
+--prewarm-ms (default 250 ms; their count is ``prewarm_steps``): under load the
+GPU clock settles only after tens of milliseconds, and a handful of warmup
+steps would time the transient instead of the steady state.
+
 Prints one JSON line. ``value`` is the attention metric 4*N^2*d*H*B / step time
 in TOPS (dense-equivalent operation count, the whole step in the denominator).
 ``roofline`` describes the dominant kernel (attn_fwd): its algorithmic
@@ -181,13 +186,16 @@ def run_peaks():
         print(json.dumps(line), flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm-ms", type=float, default=250.0,
+                    help="untimed whole steps for at least this long before the warmup steps "
+                         "(the GPU clock settles under load)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--promote", action="store_true",
@@ -213,7 +221,7 @@ def parse():
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 64K (long-context causal) forward that the default 8K line "
                          "reports beside its own")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def roofline_fracs(alg_ops: float, ms: float, traffic):
@@ -397,6 +405,25 @@ def run_cpu_baseline(p, t, target_s: float, keep=None, promote: bool = False, ad
     }
 
 
+def workload_keep(args, p):
+    """The keep ratio the step's mask uses (None: no mask), after the checks of
+    the option combinations (host only, before any GPU work)."""
+    if sum([args.promote, args.adaptive is not None, args.stripes is not None]) > 1:
+        raise SystemExit("--promote, --adaptive and --stripes are exclusive")
+    if args.low4 and not args.promote:
+        raise SystemExit("--low4 is the low path of --promote")
+    if args.adaptive is not None or args.stripes is not None:
+        keep = None
+    else:
+        keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
+    if args.patterns is not None:
+        if keep is None:
+            raise SystemExit("--patterns extends a block mask (a sparse workload or --promote)")
+        if not all(0 <= n <= 64 for n in args.patterns):
+            raise SystemExit("--patterns: NV and NS in [0, 64]")
+    return keep
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -414,22 +441,13 @@ def main():
     import bit_quantized_attention_amd as qa
     from synthetic import make_config
 
-    qa.load()
     p, t = make_config(args.config)
-    dev = torch.device("cuda:0")
-    q, k, v = (t[x].to(dev) for x in "qkv")
-    if sum([args.promote, args.adaptive is not None, args.stripes is not None]) > 1:
-        raise SystemExit("--promote, --adaptive and --stripes are exclusive")
-    if args.low4 and not args.promote:
-        raise SystemExit("--low4 is the low path of --promote")
+    keep = workload_keep(args, p)
     adaptive = args.adaptive is not None
     stripes = args.stripes is not None
-    if adaptive or stripes:
-        keep = None
-    else:
-        keep = p.sparse if (p.sparse is not None or not args.promote) else (1, 10)
-    if args.patterns is not None and keep is None:
-        raise SystemExit("--patterns extends a block mask (a sparse workload or --promote)")
+    qa.load()
+    dev = torch.device("cuda:0")
+    q, k, v = (t[x].to(dev) for x in "qkv")
     plan = qa.Plan(qa.problem(p.B, p.Hq, p.Hkv, p.N, p.d, p.dtype, p.causal), dev,
                    sparse=keep, promote=args.promote, low4=args.low4,
                    pools=True if stripes else None,
@@ -477,7 +495,7 @@ def main():
             plan.fwd(v, o)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
+    def one_step():
         plan.smooth_quant(q, k)
         if keep is not None:
             block_mask()
@@ -486,6 +504,22 @@ def main():
         if stripes:
             stripe_select()
         attention()
+
+    # The GPU's clock settles only after tens of milliseconds under load (at
+    # N = 8192 the attention kernel runs about 15 % slower over the first 25
+    # steps than after 70): whole untimed steps for at least --prewarm-ms
+    # first, synchronized every few steps so that the wall time is GPU time,
+    # then the W counted warmup steps.
+    prewarm_steps = 0
+    t_pw = time.perf_counter()
+    while (time.perf_counter() - t_pw) * 1e3 < args.prewarm_ms:
+        one_step()
+        prewarm_steps += 1
+        if prewarm_steps % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        one_step()
     torch.cuda.synchronize()
 
     # timed region: K whole steps; the attention kernel's own launches are
@@ -584,6 +618,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_steps": prewarm_steps,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -1,5 +1,5 @@
-"""The bench's operation counts against brute force, and its one-GPU guard
-(host logic, no GPU)."""
+"""The bench's operation counts against brute force, its one-GPU guard and the
+checks of its option combinations (host logic, no GPU)."""
 
 import json
 import os
@@ -8,6 +8,7 @@ import sys
 from types import SimpleNamespace
 
 import numpy as np
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
@@ -87,3 +88,21 @@ def test_roofline_fractions():
     assert abs(f["frac_blended"] - tops / (10000.0 / 3.0)) < 1e-12
     assert abs(f["hbm_frac"] - 160e6 / 0.5e-3 / 8e12) < 1e-12
     assert bench.roofline_fracs(ops, 0.5, None)["hbm_frac"] is None
+
+
+def test_option_combinations():
+    # host-side checks of the step's options, before any GPU work
+    from synthetic import make_config
+    p2, _ = make_config(1)     # dense workload (no keep ratio of its own)
+
+    def keep(*argv, p=p2):
+        return bench.workload_keep(bench.parse(list(argv)), p)
+
+    assert keep() is None
+    assert keep("--promote") == (1, 10)
+    assert keep("--promote", "--low4") == (1, 10)
+    assert keep("--promote", "--patterns", "4", "4") == (1, 10)
+    for bad in (["--low4"], ["--patterns", "4", "4"], ["--promote", "--adaptive", "0.02"],
+                ["--promote", "--patterns", "65", "0"], ["--stripes", "1.0", "--patterns", "1", "1"]):
+        with pytest.raises(SystemExit):
+            keep(*bad)
