@@ -282,9 +282,11 @@ qattn_status_t qattn_fwd_promoted(const qattn_problem_t* p, const int8_t* q_i8,
  *      [B,Hkv,d] f32 from qattn_smooth_quant; kv_idx [B,Hq,N/128,max_keep],
  *      kv_cnt [B,Hq,N/128] int32 as for qattn_fwd_promoted.
  * Out: o [B,Hq,N,d] in p->dtype; lse [B,Hq,N] f32 or NULL.
- * workspace: device scratch of at least qattn_lowbit_workspace_bytes(p)
- *      bytes, overwritten (its start holds the codes: the same layout as the
- *      low-bit mask's); not to be shared with a concurrent call.
+ * workspace: device scratch for the codes, overwritten (the layout of the
+ *      low-bit mask's workspace without its block scores:
+ *      qattn_lowbit_workspace_bytes(p) - 4*B*Hq*(N/128)*(N/64) bytes suffice,
+ *      qattn_lowbit_workspace_bytes(p) always does); not to be shared with a
+ *      concurrent call.
  * Errors: NULL for any missing pointer but lse; SHAPE/UNSUPPORTED, also
  *      UNSUPPORTED when N > 131072; ALIGN; ARG when max_keep < 1,
  *      max_keep > 2048 or the workspace is too small; DEVICE.
