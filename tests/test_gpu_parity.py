@@ -32,6 +32,10 @@ SMALL = [
                                        causal=True, seed=23, k_offset_std=2.0)),
     ("bf16-d64-causal-mqa-N512", dict(B=1, Hq=4, Hkv=1, N=512, d=64, dtype="bf16",
                                       causal=True, seed=24, k_offset_std=3.0, outliers=2)),
+    # three query heads per kv head: the dense layout takes one head per
+    # 8-wave workgroup (256 rows) instead of 4 heads x 2 slabs
+    ("f16-d128-causal-group3-N768", dict(B=2, Hq=6, Hkv=2, N=768, d=128, dtype="f16",
+                                         causal=True, seed=25, k_offset_std=3.0, outliers=2)),
 ]
 
 

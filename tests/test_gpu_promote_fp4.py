@@ -37,6 +37,9 @@ CASES = [
     ("bf16-d128-nc-N1152-keep10", dict(B=1, Hq=2, Hkv=1, N=1152, d=128, dtype="bf16",
                                        causal=False, seed=65, k_offset_std=3.0, outliers=4),
      (1, 10)),
+    ("bf16-d64-causal-group3-B2-N768-keep10", dict(B=2, Hq=6, Hkv=2, N=768, d=64,
+                                                   dtype="bf16", causal=True, seed=60,
+                                                   k_offset_std=3.0, outliers=2), (1, 10)),
 ]
 
 
