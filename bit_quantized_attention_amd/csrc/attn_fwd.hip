@@ -26,13 +26,14 @@
 // lane 4 consecutive keys of one channel.
 //
 // Pipeline (one barrier per tile; each stage of K tile, its scale and V tile
-// is one LDS object): dense workgroups run the P V products of tile t-1
+// is one LDS object): the workgroups run the P V products of tile t-1
 // inside the softmax of tile t, so each wave feeds its matrix unit while its
-// vector unit works (four stages); sparse workgroups run S, the softmax and
-// P V of a tile in sequence (three stages) and the waves sharing a SIMD
-// overlap each other's work. Q fragments stay in registers; every K tile
-// carries its scale in a small tail of its stage (no scalar loads in the
-// loop).
+// vector unit works (dense: four stages; sparse: three, so that two
+// workgroups fit a CU). The promoted and gathered variants run S, the
+// softmax and P V of a tile in sequence (three stages) and the waves sharing
+// a SIMD overlap each other's work. Q fragments stay in registers; every K
+// tile carries its scale in a small tail of its stage (no scalar loads in
+// the loop).
 //
 // Online softmax reference: a row's exponent reference m moves only when the
 // tile's running max exceeds it by more than kTau (log2 units); otherwise P is
@@ -196,8 +197,8 @@ void attn_fwd_kernel(FwdArgs a) {
   using el_t = typename MM::el_t;
   using G = Geo<D>;
   constexpr int RW = 32 * QB;
-  // lagged P V (dense workgroups)
-  constexpr bool kLAG = !SPARSE && NW * QB >= 8;
+  // lagged P V (dense 8-wave workgroups and the plain block-sparse layout)
+  constexpr bool kLAG = (!SPARSE && NW * QB >= 8) || (SPARSE && !PROMOTE && !GATHER);
   // promoted path: sparse layout (one 128-row query block per workgroup),
   // one 32-query block per wave
   static_assert(!PROMOTE || (SPARSE && QB == 1), "promoted path: sparse layout, QB = 1");
@@ -1118,15 +1119,20 @@ void attn_fwd_kernel(FwdArgs a) {
   // iteration issues the same loads. The loops are unrolled NBUF times so
   // that every buffer is named at compile time.
   //
-  // Lagged P V (dense 8-wave workgroups): iteration it runs the P V products
-  // of tile it-1 inside the softmax of tile it, four matrix instructions per
-  // 16-key group of exponentials, so each wave keeps its matrix unit busy
-  // while its vector unit works (P of consecutive tiles alternates between
-  // two register sets; the first iteration multiplies a copy of tile 0's V
-  // by a zero P). V(it-1) is still read in iteration it, so the prefetch distance is
-  // NBUF-2. Otherwise (sparse) each wave runs S, the softmax and P V of a
-  // tile in sequence and the waves sharing a SIMD overlap each other's work.
-  static_assert(!kLAG || NBUF == 4 || NBUF == 6, "lagged products: four or six stages");
+  // Lagged P V: iteration it runs the P V products of tile it-1 inside the
+  // softmax of tile it, four matrix instructions per 16-key group of
+  // exponentials, so each wave keeps its matrix unit busy while its vector
+  // unit works (P of consecutive tiles alternates between two register sets;
+  // the first iteration multiplies a copy of tile 0's V by a zero P).
+  // V(it-1) is still read in iteration it, so the prefetch distance is
+  // NBUF-2: two tiles in the dense layout, one in the block-sparse layout,
+  // whose three stages keep two workgroups per CU (four stages and one
+  // workgroup measured slower). With an odd NBUF the loops are unrolled 2 NBUF
+  // times, so that P's register set stays a compile-time choice. Otherwise
+  // (promoted, gathered) each wave runs S, the softmax and P V of a tile in
+  // sequence and the waves sharing a SIMD overlap each other's work.
+  static_assert(!kLAG || NBUF == 3 || NBUF == 4 || NBUF == 6, "lagged products: three, four or six stages");
+  constexpr int UNR = (kLAG && (NBUF & 1)) ? 2 * NBUF : NBUF;
   // prefetch distance (tiles) and the furthest tile the next iteration reads
   constexpr int PD = kLAG ? NBUF - 2 : NBUF - 1;
   static_for<0, PD>([&](auto j) {
@@ -1137,8 +1143,8 @@ void attn_fwd_kernel(FwdArgs a) {
   // lagged: the first iteration's "previous" V buffer gets tile 0's V too, so
   // that its zero P meets finite values (and the buffer is named at compile
   // time: a runtime choice of LDS buffer makes the compiler wait for every
-  // load in flight before reading it)
-  if constexpr (kLAG) load_v(tile_of(0), vbuf(std::integral_constant<int, NBUF - 1>{}));
+  // load in flight before reading it); an empty kept list reads tile 0
+  if constexpr (kLAG) load_v(ntiles > 0 ? tile_of(0) : 0, vbuf(std::integral_constant<int, NBUF - 1>{}));
   wait_all();
   __syncthreads();
 
@@ -1172,7 +1178,8 @@ void attn_fwd_kernel(FwdArgs a) {
     v16i s[2][QB];
     float alpha = 0.0f;
     if constexpr (kLAG) {
-      // (NBUF is even, so J and it have the same parity)
+      // (NBUF is even or the loops run 2 NBUF steps, so J and it have the
+      // same parity)
       const op_t (&p_in)[2][QB][2] = (J & 1) ? p_even : p_odd;
       op_t (&p_out)[2][QB][2] = (J & 1) ? p_odd : p_even;
       const int8_t* vp = vbuf(prv);
@@ -1255,15 +1262,15 @@ void attn_fwd_kernel(FwdArgs a) {
     }
     barrier();
   };
-  for (int base = 0; base < n_plain; base += NBUF) {
-    static_for<0, NBUF>([&](auto j) {
+  for (int base = 0; base < n_plain; base += UNR) {
+    static_for<0, UNR>([&](auto j) {
       if (base + (int)j < n_plain) step(j, base + (int)j, kNo);
     });
   }
   // the masked tiles (the last few), one step each
   for (int it = n_plain; it < ntiles; ++it) {
-    static_for<0, NBUF>([&](auto j) {
-      if (it % NBUF == (int)j) step(j, it, kYes);
+    static_for<0, UNR>([&](auto j) {
+      if (it % UNR == (int)j) step(j, it, kYes);
     });
   }
   // promoted path: the halves of the promoted tiles, after the INT8 tiles
@@ -1333,8 +1340,8 @@ void attn_fwd_kernel(FwdArgs a) {
   if constexpr (kLAG) {
     // the last tile's P V (its buffer has landed and is not reloaded)
     if (wave_live && ntiles > 0) {
-      static_for<0, NBUF>([&](auto j) {
-        if ((ntiles - 1) % NBUF == (int)j) pv(vbuf(j), (j & 1) ? p_odd : p_even);
+      static_for<0, UNR>([&](auto j) {
+        if ((ntiles - 1) % UNR == (int)j) pv(vbuf(j), (j & 1) ? p_odd : p_even);
       });
     }
   }
