@@ -1,10 +1,11 @@
 // Quantized attention forward on gfx950 matrix cores.
 //
 // Work decomposition. A wave owns 32 query rows of one query head (one
-// 32-column MFMA block). Dense: a workgroup of 8 waves takes g4 = 4, 2 or 1
-// query heads of one kv head (the largest that divides the group size) times
-// 8/g4 consecutive 32-row slabs, so all 8 waves share every K/V tile they
-// stage (GQA group 4: four heads x the same 64 rows). Sparse: a workgroup of
+// 32-column MFMA block). Dense: a workgroup of NW waves (8 at d = 128, 4 at
+// d = 64) takes g4 = 4, 2 or 1 query heads of one kv head (the largest that
+// divides the group size) times NW/g4 consecutive 32-row slabs, so all its
+// waves share every K/V tile they stage (d = 128, GQA group 4: four heads x
+// the same 64 rows). Sparse: a workgroup of
 // 4 waves takes one 128-row query block of one head; its kept list is the
 // workgroup's tile list. Consecutive workgroups map to distinct kv heads, so
 // blockIdx % 8 (the XCD) keeps each kv head on one XCD's L2; under causal
@@ -28,8 +29,8 @@
 // Pipeline (one barrier per tile; each stage of K tile, its scale and V tile
 // is one LDS object): the workgroups run the P V products of tile t-1
 // inside the softmax of tile t, so each wave feeds its matrix unit while its
-// vector unit works (dense: four stages; sparse: three, so that two
-// workgroups fit a CU). The promoted and gathered variants run S, the
+// vector unit works (dense d = 128: four stages; dense d = 64 and sparse:
+// three, so that three or two workgroups fit a CU). The promoted and gathered variants run S, the
 // softmax and P V of a tile in sequence (three stages) and the waves sharing
 // a SIMD overlap each other's work. Q fragments stay in registers; every K
 // tile carries its scale in a small tail of its stage (no scalar loads in
@@ -61,6 +62,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kKT = 64;             // keys per tile
+
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
 // The INT8 product accumulates onto the bit pattern of 1.5 * 2^23: every
 // |S| < 2^22 (d * 127^2 at most) then reads, as an fp32 number, exactly
@@ -197,8 +199,8 @@ void attn_fwd_kernel(FwdArgs a) {
   using el_t = typename MM::el_t;
   using G = Geo<D>;
   constexpr int RW = 32 * QB;
-  // lagged P V (dense 8-wave workgroups and the plain block-sparse layout)
-  constexpr bool kLAG = (!SPARSE && NW * QB >= 8) || (SPARSE && !PROMOTE && !GATHER);
+  // lagged P V (the dense and the plain block-sparse layouts)
+  constexpr bool kLAG = !PROMOTE && !GATHER;
   // promoted path: sparse layout (one 128-row query block per workgroup),
   // one 32-query block per wave
   static_assert(!PROMOTE || (SPARSE && QB == 1), "promoted path: sparse layout, QB = 1");
@@ -1125,9 +1127,10 @@ void attn_fwd_kernel(FwdArgs a) {
   // unit works (P of consecutive tiles alternates between two register sets;
   // the first iteration multiplies a copy of tile 0's V by a zero P).
   // V(it-1) is still read in iteration it, so the prefetch distance is
-  // NBUF-2: two tiles in the dense layout, one in the block-sparse layout,
-  // whose three stages keep two workgroups per CU (four stages and one
-  // workgroup measured slower). With an odd NBUF the loops are unrolled 2 NBUF
+  // NBUF-2: two tiles in the d = 128 dense layout (four stages), one in the
+  // d = 64 dense and the block-sparse layouts, whose three stages keep three
+  // or two workgroups per CU (four stages and one workgroup measured
+  // slower). With an odd NBUF the loops are unrolled 2 NBUF
   // times, so that P's register set stays a compile-time choice. Otherwise
   // (promoted, gathered) each wave runs S, the softmax and P V of a tile in
   // sequence and the waves sharing a SIMD overlap each other's work.
@@ -1216,6 +1219,11 @@ void attn_fwd_kernel(FwdArgs a) {
         auto lagged_pv = [&](auto qbc, auto gc) {
           constexpr int qb = decltype(qbc)::value;
           constexpr int g = decltype(gc)::value;
+          // each group's products stay at the start of its own 16-key group
+          // of exponentials: left free, the compiler hoists all of them to
+          // the top of the tile and the second half of the softmax runs with
+          // the matrix unit idle (1.5 % at d = 64, 0.5 % at d = 128)
+          __builtin_amdgcn_sched_barrier(0);
           if constexpr (kSplitQK && g < 2) {
             // k-steps [g*KS/2, (g+1)*KS/2) of the kb = 1 product
 #pragma unroll
@@ -1377,7 +1385,10 @@ void attn_fwd_kernel(FwdArgs a) {
 }
 
 #ifndef QATTN_NW_DENSE64
-#define QATTN_NW_DENSE64 8
+#define QATTN_NW_DENSE64 4
+#endif
+#ifndef QATTN_WPE_DENSE_SMALL
+#define QATTN_WPE_DENSE_SMALL 3
 #endif
 #ifndef QATTN_NW_DENSE
 #define QATTN_NW_DENSE 8
@@ -1393,11 +1404,15 @@ template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_dc(const FwdArgs& a, bool sparse, hipStream_t stream) {
   constexpr int QB = QATTN_QB;     // 32-query blocks per wave (sparse)
   constexpr int QBD = QATTN_QB_DENSE;  // 32-query blocks per wave (dense)
-  // dense: one workgroup of NW_DENSE waves per CU (NW_DENSE / 4 waves per
-  // SIMD), 8 query blocks of 32 rows in all; sparse: one 128-row query block
-  // per 4-wave workgroup, two workgroups per CU
+  // dense, d = 128: one 8-wave workgroup per CU (two waves per SIMD sharing
+  // each staged tile); dense, d = 64: three 4-wave workgroups per CU, so that
+  // the three waves on a SIMD pass independent barriers and one wave's
+  // softmax overlaps another's products (5 % faster than one 8-wave
+  // workgroup at the 4K non-causal d = 64 workload; the same split at
+  // d = 128 was 1.3 % slower); sparse: one 128-row query block per 4-wave
+  // workgroup, two workgroups per CU
   constexpr int NW_DENSE = (D == 64 ? QATTN_NW_DENSE64 : QATTN_NW_DENSE) / QBD;
-  constexpr int WPE_DENSE = NW_DENSE / 4;
+  constexpr int WPE_DENSE = NW_DENSE >= 8 ? NW_DENSE / 4 : QATTN_WPE_DENSE_SMALL;
   constexpr int NW_SPARSE = 128 / (32 * QB);
   static_assert(NW_DENSE % 4 == 0, "whole waves per SIMD");
   if (sparse) {
