@@ -1190,12 +1190,12 @@ void attn_fwd_kernel(FwdArgs a) {
       // four groups of V(t-1) at once, each set shared by the QB blocks
       constexpr int NVS = QB == 1 ? 2 : 4;
       op_t vset[NVS][G::DB];
-      // QB = 1, d = 128: the second 32-key block's INT8 products (kb = 1) run
-      // inside the first two softmax groups, which only read the first
-      // block's S: the matrix unit then has work while the softmax starts,
-      // instead of a phase of products with the vector unit idle. (d = 64 has
-      // two such products per block, too few to gain: 1 % slower measured.)
-      constexpr bool kSplitQK = QB == 1 && D == 128;
+      // QB = 1: the second 32-key block's INT8 products (kb = 1) run inside
+      // the first two softmax groups, which only read the first block's S:
+      // the matrix unit then has work while the softmax starts, instead of a
+      // phase of products with the vector unit idle (d = 64: one product per
+      // group, 0.9 % faster in the three-workgroup layout)
+      constexpr bool kSplitQK = QB == 1;
       v4i kf1[G::KS];
       if (wave_live) {
         alpha = alpha_q * tile_kscale(kbuf(cur));
