@@ -36,6 +36,12 @@ SMALL = [
     # 8-wave workgroup (256 rows) instead of 4 heads x 2 slabs
     ("f16-d128-causal-group3-N768", dict(B=2, Hq=6, Hkv=2, N=768, d=128, dtype="f16",
                                          causal=True, seed=25, k_offset_std=3.0, outliers=2)),
+    # d = 64 dense runs 4-wave workgroups: two query heads x 64 rows (group 2)
+    # and one head x 128 rows (group 3, causal, N/128 odd)
+    ("bf16-d64-causal-gqa2-N384", dict(B=1, Hq=4, Hkv=2, N=384, d=64, dtype="bf16",
+                                       causal=True, seed=26, k_offset_std=3.0, outliers=2)),
+    ("f16-d64-causal-group3-N640", dict(B=1, Hq=6, Hkv=2, N=640, d=64, dtype="f16",
+                                        causal=True, seed=27, k_offset_std=2.0)),
 ]
 
 
