@@ -42,6 +42,12 @@ SMALL = [
                                        causal=True, seed=26, k_offset_std=3.0, outliers=2)),
     ("f16-d64-causal-group3-N640", dict(B=1, Hq=6, Hkv=2, N=640, d=64, dtype="f16",
                                         causal=True, seed=27, k_offset_std=2.0)),
+    # the shortest sequences the library takes (one 128-row query block, two
+    # key tiles): most waves of a workgroup have no rows
+    ("f16-d64-causal-N128", dict(B=1, Hq=2, Hkv=1, N=128, d=64, dtype="f16", causal=True,
+                                 seed=28, k_offset_std=2.0)),
+    ("bf16-d128-nc-mqa4-N128", dict(B=1, Hq=4, Hkv=1, N=128, d=128, dtype="bf16",
+                                    causal=False, seed=29, k_offset_std=3.0, outliers=2)),
 ]
 
 
