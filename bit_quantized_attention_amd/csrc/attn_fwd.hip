@@ -30,9 +30,9 @@
 // is one LDS object): the workgroups run the P V products of tile t-1
 // inside the softmax of tile t, so each wave feeds its matrix unit while its
 // vector unit works (dense d = 128: four stages; dense d = 64 and sparse:
-// three, so that three or two workgroups fit a CU). The promoted and gathered variants run S, the
-// softmax and P V of a tile in sequence (three stages) and the waves sharing
-// a SIMD overlap each other's work. Q fragments stay in registers; every K
+// three, so that three or two workgroups fit a CU). The promoted and
+// gathered variants run S, the softmax and P V of a tile in sequence (three
+// stages) and the waves sharing a SIMD overlap each other's work. Q fragments stay in registers; every K
 // tile carries its scale in a small tail of its stage (no scalar loads in
 // the loop).
 //
@@ -62,7 +62,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kKT = 64;             // keys per tile
-
 constexpr float kTau = QATTN_SOFTMAX_REF_THRESHOLD;  // log2 units
 // The INT8 product accumulates onto the bit pattern of 1.5 * 2^23: every
 // |S| < 2^22 (d * 127^2 at most) then reads, as an fp32 number, exactly
@@ -1130,8 +1129,8 @@ void attn_fwd_kernel(FwdArgs a) {
   // NBUF-2: two tiles in the d = 128 dense layout (four stages), one in the
   // d = 64 dense and the block-sparse layouts, whose three stages keep three
   // or two workgroups per CU (four stages and one workgroup measured
-  // slower). With an odd NBUF the loops are unrolled 2 NBUF
-  // times, so that P's register set stays a compile-time choice. Otherwise
+  // slower). With an odd NBUF the loops are unrolled 2 NBUF times, so that
+  // P's register set stays a compile-time choice. Otherwise
   // (promoted, gathered) each wave runs S, the softmax and P V of a tile in
   // sequence and the waves sharing a SIMD overlap each other's work.
   static_assert(!kLAG || NBUF == 3 || NBUF == 4 || NBUF == 6, "lagged products: three, four or six stages");
